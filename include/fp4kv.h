@@ -1,0 +1,249 @@
+/*
+ * fp4kv: the hot path of CSA2-style sparse attention over an FP4 main-KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages on DeepSeek V4.1-Flash's KV cache):
+ *   [G] "DeepSeek V4.1 Flash KV Cache: 890 Bytes per Token Explained"
+ *       (paragraphs on CSA2 modes, the hierarchical sparse indexer, FP4 main KV,
+ *       SWA Bounded Replay; the page has no section headings).
+ *   [T] "890 bytes per token: how DeepSeek V4.1-Flash's KV cache works",
+ *       sections "Mechanism 3: FP4 KV via quantization-aware training" and
+ *       "Mechanism 4: the hierarchical sparse indexer".
+ *   [N] "DeepSeek-V4.1-Flash: 890 Bytes Per Token, 437x Smaller KV Cache",
+ *       sections "CSA2: Sharing Main KV, Indexer K, and Top-K Indices Across
+ *       Layers", "FP4 KV Quantization and Cache Lifetime Management" and
+ *       "Causal Encoder-Decoder and Prefill Halving".
+ *
+ * How a model calls this library, one layer at a time ([N] "CSA2: ..."):
+ *   Full layer     -> fp4kv_index_full, then fp4kv_sparse_attn_{decode,prefill}
+ *   Reindex layer  -> fp4kv_index_reindex on the Full layer's pool, then attention
+ *   Reuse layer    -> no indexer call; attention with the indices it is handed
+ * Every layer attends with its own main Q and its own sliding-window KV.
+ * New main-KV rows enter the cache through fp4kv_quantize_append.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) point to GPU memory; all others are host values.
+ *     The caller owns every buffer. The library never allocates or frees, and
+ *     keeps no pointer after a call returns.
+ *   - Inputs are read-only. Work is enqueued on `stream` (a hipStream_t; NULL =
+ *     the default stream) and the call returns without waiting for it.
+ *   - Grids are sized from host scalars only; device-resident counts and
+ *     positions are read by the kernels, which clamp them to the sizes given
+ *     here so that no access leaves the buffers described.
+ *   - Arguments are checked before anything is launched. On error nothing is
+ *     launched, a negative status is returned and fp4kv_last_error() describes
+ *     it (a thread-local string, valid until the next call on that thread).
+ *     FP4KV_ERR_HIP reports a launch failure; outputs are then undefined.
+ *   - Results are deterministic: identical inputs give identical bits.
+ *   - Positions are relative to the first row of their sequence. Index lists are
+ *     ascending; entries past the count are -1.
+ *   - bf16 is bfloat16 stored as 16-bit words.
+ */
+#ifndef FP4KV_H
+#define FP4KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fp4kv_status;
+
+enum {
+    FP4KV_OK = 0,
+    FP4KV_ERR_NULL = -1,        /* a required pointer is NULL */
+    FP4KV_ERR_SHAPE = -2,       /* a size or layout argument is out of range */
+    FP4KV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+    FP4KV_ERR_UNSUPPORTED = -4, /* valid, but not a shape these kernels implement */
+    FP4KV_ERR_HIP = -5          /* the HIP runtime reported an error */
+};
+
+#define FP4KV_ABI_VERSION 1
+
+/* Version of this interface (FP4KV_ABI_VERSION of the built library). */
+int32_t fp4kv_abi_version(void);
+
+/* Description of the last failed call on this thread ("" if none). */
+const char* fp4kv_last_error(void);
+
+/*
+ * FP4 quantize-append of main-KV rows.
+ * [G] FP4 main KV paragraph, [N] "FP4 KV Quantization and Cache Lifetime
+ * Management": E2M1 values with one E4M3 scale per 16 channels and no global
+ * scale.
+ *
+ * For each source row i and each group g of 16 channels:
+ *   scale code  = E4M3 (FN: bias 7, max 448, no inf) value nearest amax/6,
+ *                 ties to the even code, saturating at 448; subnormal scales
+ *                 are kept, amax/6 <= 2^-10 gives 0;
+ *   value code  = sign bit of x, then the E2M1 magnitude nearest |x|/scale
+ *                 (ties to the even code, saturating at 6; 0 if the scale is 0).
+ * Codes are exact (no floating-point rounding of the ratio is involved).
+ *
+ *   src       (device) bf16 [n_rows, C], row-major.
+ *   n_rows    rows to append (0 is allowed and launches nothing).
+ *   C         channels per row, a positive multiple of 32.
+ *   dst_rows  (device) int64 [n_rows]: destination row of each source row, or
+ *             NULL to write rows dst_start .. dst_start+n_rows-1. Destination
+ *             rows outside [0, cap_rows) are skipped (not written).
+ *   codes     (device) uint8 [cap_rows, C/2]: channel 2j in the low nibble of
+ *             byte j, channel 2j+1 in the high nibble.
+ *   scales    (device) uint8 [cap_rows, C/16]: E4M3 scale codes.
+ *   Together 288 bytes per row at C = 512.
+ * Errors: NULL src/codes/scales; C not a positive multiple of 32; n_rows < 0;
+ * with dst_rows NULL, dst_start < 0 or dst_start + n_rows > cap_rows.
+ */
+fp4kv_status fp4kv_quantize_append(const void* src, int64_t n_rows, int32_t C,
+                                   const int64_t* dst_rows, int64_t dst_start,
+                                   uint8_t* codes, uint8_t* scales, int64_t cap_rows,
+                                   void* stream);
+
+/*
+ * Workspace bytes fp4kv_index_full needs for n_q queries whose positions are
+ * below max_ctx (token scores and block maxima, fp32).
+ */
+size_t fp4kv_index_workspace_bytes(int32_t n_q, int64_t max_ctx, int32_t block);
+
+/*
+ * Full-mode indexer: score every visible token, keep the best blocks as the
+ * candidate pool, then the best tokens inside the pool.
+ * [G] hierarchical sparse indexer paragraph (pool of 2,048 blocks of 8 tokens,
+ * each query keeps its best 512); [T] "Mechanism 4"; [N] "CSA2: ...", Full
+ * bullet.
+ *
+ * The pages leave the scoring rule open. This library computes, for query i at
+ * position p and each token t <= p of its sequence,
+ *     score(t) = sum_h w[i,h] * max(0, sum_d q[i,h,d] * k[t,d])   (fp32)
+ * (one indexer key per token, shared by the heads), the score of block b as
+ * the max over its visible tokens 8b..min(8b+7, p), the pool as the
+ * min(P, p/8+1) best blocks, and the selection as the min(k, #visible pool
+ * positions) best positions inside the pool. Ranking is by score descending,
+ * ties to the lower block id / position. With integer-valued bf16 inputs whose
+ * partial sums stay below 2^24 the scores are exact.
+ *
+ *   idx_q       (device) bf16 [n_q, H, D]
+ *   w           (device) fp32 [n_q, H]
+ *   idx_k       (device) bf16 [total_rows, D]: indexer keys of all sequences.
+ *   seq_start   (device) int64 [ceil(n_q / q_per_seq)]: first row of each
+ *               sequence; query i belongs to sequence i / q_per_seq.
+ *   q_pos       (device) int32 [n_q]: position of each query (its causal
+ *               limit; decode: context length - 1). Clamped to [0, max_ctx-1];
+ *               rows at or past total_rows are treated as not visible.
+ *   H, D        H in {4, 8, 16}; D in {64, 128}.
+ *   max_ctx     host bound: every q_pos < max_ctx (sizes the grid).
+ *   block       tokens per block; must be 8.
+ *   P, k        pool blocks and kept tokens; 1 <= P, 1 <= k <= P*block,
+ *               P*block <= 16384.
+ *   pool_out    (device) int32 [n_q, P]; n_pool (device) int32 [n_q].
+ *   idx_out     (device) int32 [n_q, k]; n_idx  (device) int32 [n_q].
+ *   workspace   (device) at least fp4kv_index_workspace_bytes(n_q, max_ctx, block).
+ * The prefill case is a single sequence with q_per_seq = n_q queries at
+ * consecutive positions; it runs the same computation.
+ */
+fp4kv_status fp4kv_index_full(const void* idx_q, const float* w, const void* idx_k,
+                              int64_t total_rows, const int64_t* seq_start,
+                              const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                              int32_t H, int32_t D, int64_t max_ctx, int32_t block,
+                              int32_t P, int32_t k, int32_t* pool_out, int32_t* n_pool,
+                              int32_t* idx_out, int32_t* n_idx, void* workspace,
+                              size_t ws_bytes, void* stream);
+
+/* Workspace bytes fp4kv_index_reindex needs (pool token scores, fp32). */
+size_t fp4kv_reindex_workspace_bytes(int32_t n_q, int32_t P, int32_t block);
+
+/*
+ * Reindex-mode indexer: rescore an inherited pool with this layer's own
+ * indexer Q and weights, then keep the best tokens.
+ * [N] "CSA2: ...", Reindex bullet: reuses the preceding Full layer's main KV
+ * and indexer K and applies its own indexer Q to rescore the candidate pool;
+ * [G] hierarchical sparse indexer paragraph: deeper layers search the pool.
+ *
+ * Same scoring and ranking rule as fp4kv_index_full, over the visible
+ * positions (<= q_pos) of pool blocks pool[i, 0 .. n_pool[i]-1] only (n_pool
+ * clamped to [0, P]; block ids outside the sequence are ignored). Selects
+ * min(k, #visible pool positions) positions, ascending.
+ *   idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D:
+ *               as for fp4kv_index_full (this layer's own idx_q and w).
+ *   pool        (device) int32 [n_q, P] ascending block ids; n_pool (device) [n_q].
+ *   idx_out     (device) int32 [n_q, k]; n_idx (device) int32 [n_q].
+ *   workspace   (device) at least fp4kv_reindex_workspace_bytes(n_q, P, block).
+ */
+fp4kv_status fp4kv_index_reindex(const void* idx_q, const float* w, const void* idx_k,
+                                 int64_t total_rows, const int64_t* seq_start,
+                                 const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                                 int32_t H, int32_t D, const int32_t* pool,
+                                 const int32_t* n_pool, int32_t block, int32_t P, int32_t k,
+                                 int32_t* idx_out, int32_t* n_idx, void* workspace,
+                                 size_t ws_bytes, void* stream);
+
+/*
+ * Workspace bytes the attention entry points need for n_q queries (partial
+ * softmax states when a query's rows are split over several workgroups; may
+ * be 0).
+ */
+size_t fp4kv_attn_workspace_bytes(int32_t n_q, int32_t Hq, int32_t C, int32_t k, int32_t W);
+
+/*
+ * Sparse attention over selected FP4 main-KV rows plus a sliding-window branch,
+ * merged by log-sum-exp; one query per sequence (decode).
+ * [T] "Mechanism 4" (attention runs over the selected candidates); [N] "CSA2:
+ * ..." (every layer uses its own main Q and SWA KV) and "Causal
+ * Encoder-Decoder and Prefill Halving" (a 128-token sliding window).
+ *
+ * For query b at position p = q_pos[b] and every head h:
+ *   sparse branch: rows j = idx[b, 0 .. n_idx[b]-1] (n_idx clamped to [0, k];
+ *     positions outside [0, p] or past total_rows are skipped), dequantised
+ *     from (codes, scales); logits scale * q[b,h,:] . row; keys = values = the
+ *     dequantised row. Softmax over the rows gives (o_s, lse_s).
+ *   window branch: the last n_w = min(W, p+1) rows of swa_k[b] / swa_v[b]
+ *     (row W-1 is position p), softmax -> (o_w, lse_w).
+ *   out = (e^lse_s o_s + e^lse_w o_w) / (e^lse_s + e^lse_w); lse = log of the
+ *     denominator (natural log). An empty sparse branch contributes nothing.
+ *
+ *   q          (device) bf16 [B, Hq, C]
+ *   codes      (device) uint8 [total_rows, C/2]; scales (device) uint8 [total_rows, C/16]
+ *   seq_start  (device) int64 [B]: first main-KV row of each query's sequence.
+ *   idx        (device) int32 [B, k]; n_idx (device) int32 [B]
+ *   swa_k, swa_v (device) bf16 [B, W, C]
+ *   q_pos      (device) int32 [B]
+ *   Hq in {16, 32, 64}; C = 512; 1 <= k <= 16384; 1 <= W <= 16384.
+ *   scale      softmax scale (finite).
+ *   out        (device) fp32 [B, Hq, C]; lse (device) fp32 [B, Hq], or NULL.
+ *   workspace  (device) at least fp4kv_attn_workspace_bytes(B, Hq, C, k, W).
+ * Numerics: logits and outputs accumulate in fp32; dequantised rows are exact
+ * in bf16 and P enters the P.V product as a bf16 hi + lo pair.
+ */
+fp4kv_status fp4kv_sparse_attn_decode(const void* q, const uint8_t* codes,
+                                      const uint8_t* scales, int64_t total_rows,
+                                      const int64_t* seq_start, const int32_t* idx,
+                                      const int32_t* n_idx, const void* swa_k,
+                                      const void* swa_v, const int32_t* q_pos, int32_t B,
+                                      int32_t Hq, int32_t C, int32_t k, int32_t W,
+                                      float scale, float* out, float* lse, void* workspace,
+                                      size_t ws_bytes, void* stream);
+
+/*
+ * The same attention for a prefill chunk: T queries of one sequence at
+ * positions pos0 .. pos0+T-1 (first main-KV row seq_start, a host value).
+ * The window buffer is shared: swa_k / swa_v (device) bf16 [T+W-1, C], row r
+ * holding position pos0-W+1+r; query i uses rows i+W-n_w .. i+W-1 with
+ * n_w = min(W, pos0+i+1). Rows for negative positions are never read.
+ * Other arguments as for fp4kv_sparse_attn_decode, with B replaced by T
+ * (workspace: fp4kv_attn_workspace_bytes(T, Hq, C, k, W)); pos0 >= 0.
+ */
+fp4kv_status fp4kv_sparse_attn_prefill(const void* q, const uint8_t* codes,
+                                       const uint8_t* scales, int64_t total_rows,
+                                       int64_t seq_start, const int32_t* idx,
+                                       const int32_t* n_idx, const void* swa_k,
+                                       const void* swa_v, int32_t pos0, int32_t T,
+                                       int32_t Hq, int32_t C, int32_t k, int32_t W,
+                                       float scale, float* out, float* lse, void* workspace,
+                                       size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4KV_H */

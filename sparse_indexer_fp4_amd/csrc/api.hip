@@ -1,0 +1,290 @@
+// C ABI of libfp4kv: argument checks, workspace sizing, grid sizing from host
+// scalars, and kernel launches on the caller's stream. The declarations and
+// their contracts are in include/fp4kv.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/fp4kv.h"
+#include "kernels.h"
+
+
+namespace {
+
+thread_local std::string g_error;
+
+fp4kv_status fail(fp4kv_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+fp4kv_status ok() {
+  g_error.clear();
+  return FP4KV_OK;
+}
+
+fp4kv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(FP4KV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t nblk_of(int64_t max_ctx, int block) { return (max_ctx + block - 1) / block; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t fp4kv_abi_version(void) { return FP4KV_ABI_VERSION; }
+
+const char* fp4kv_last_error(void) { return g_error.c_str(); }
+
+fp4kv_status fp4kv_quantize_append(const void* src, int64_t n_rows, int32_t C, const int64_t* dst_rows,
+                                   int64_t dst_start, uint8_t* codes, uint8_t* scales, int64_t cap_rows,
+                                   void* stream) {
+  if (!src || !codes || !scales) return fail(FP4KV_ERR_NULL, "quantize_append: src, codes and scales must be non-NULL");
+  if (C <= 0 || C % 32 != 0) return fail(FP4KV_ERR_SHAPE, "quantize_append: C=%d must be a positive multiple of 32", C);
+  if (n_rows < 0 || cap_rows < 0) return fail(FP4KV_ERR_SHAPE, "quantize_append: n_rows and cap_rows must be >= 0");
+  if (!dst_rows && (dst_start < 0 || dst_start + n_rows > cap_rows))
+    return fail(FP4KV_ERR_SHAPE, "quantize_append: rows [%lld, %lld) outside the cache of %lld rows",
+                (long long)dst_start, (long long)(dst_start + n_rows), (long long)cap_rows);
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(codes) & 7u))
+    return fail(FP4KV_ERR_SHAPE, "quantize_append: src must be 16-byte and codes 8-byte aligned");
+  if (n_rows == 0) return ok();
+  return hip_status(fp4kv::launch_quantize_append(src, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows,
+                                                  static_cast<hipStream_t>(stream)),
+                    "quantize_append");
+}
+
+size_t fp4kv_index_workspace_bytes(int32_t n_q, int64_t max_ctx, int32_t block) {
+  if (n_q <= 0 || max_ctx <= 0 || block <= 0) return 0;
+  return align_up((size_t)n_q * max_ctx * sizeof(float)) +
+         align_up((size_t)n_q * nblk_of(max_ctx, block) * sizeof(float));
+}
+
+size_t fp4kv_reindex_workspace_bytes(int32_t n_q, int32_t P, int32_t block) {
+  if (n_q <= 0 || P <= 0 || block <= 0) return 0;
+  return align_up((size_t)n_q * P * block * sizeof(float));
+}
+
+size_t fp4kv_attn_workspace_bytes(int32_t n_q, int32_t Hq, int32_t C, int32_t k, int32_t W) {
+  if (n_q <= 0 || Hq <= 0 || C != 512 || k <= 0 || W <= 0) return 0;
+  return fp4kv::attn_workspace_bytes(n_q, Hq, k, W);
+}
+
+static fp4kv_status check_indexer_common(const char* fn, const void* idx_q, const float* w, const void* idx_k,
+                                         int64_t total_rows, const int64_t* seq_start, const int32_t* q_pos,
+                                         int32_t n_q, int32_t q_per_seq, int32_t H, int32_t D, int32_t block,
+                                         int32_t P, int32_t k, const int32_t* idx_out, const int32_t* n_idx) {
+  if (!idx_q || !w || !idx_k || !seq_start || !q_pos || !idx_out || !n_idx)
+    return fail(FP4KV_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (n_q < 0 || q_per_seq < 1 || total_rows < 0) return fail(FP4KV_ERR_SHAPE, "%s: n_q >= 0, q_per_seq >= 1 and total_rows >= 0 required", fn);
+  if (H <= 0 || D <= 0 || D % 8 != 0) return fail(FP4KV_ERR_SHAPE, "%s: H=%d, D=%d (D must be a positive multiple of 8)", fn, H, D);
+  if (!fp4kv::scan_supported(H, D)) return fail(FP4KV_ERR_UNSUPPORTED, "%s: H=%d, D=%d not implemented (H in {4,8,16}, D in {64,128})", fn, H, D);
+  if (block != 8) return fail(FP4KV_ERR_UNSUPPORTED, "%s: block=%d (only 8 is implemented)", fn, block);
+  if (P < 1 || k < 1) return fail(FP4KV_ERR_SHAPE, "%s: P=%d and k=%d must be >= 1", fn, P, k);
+  if ((int64_t)P * block > 16384) return fail(FP4KV_ERR_UNSUPPORTED, "%s: P*block=%lld exceeds 16384", fn, (long long)P * block);
+  if (k > P * block) return fail(FP4KV_ERR_SHAPE, "%s: k=%d exceeds P*block=%d", fn, k, P * block);
+  if (!aligned16(idx_k) || !aligned16(idx_q)) return fail(FP4KV_ERR_SHAPE, "%s: idx_q and idx_k must be 16-byte aligned", fn);
+  return FP4KV_OK;
+}
+
+fp4kv_status fp4kv_index_full(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
+                              const int64_t* seq_start, const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                              int32_t H, int32_t D, int64_t max_ctx, int32_t block, int32_t P, int32_t k,
+                              int32_t* pool_out, int32_t* n_pool, int32_t* idx_out, int32_t* n_idx,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  fp4kv_status st = check_indexer_common("index_full", idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq,
+                                         H, D, block, P, k, idx_out, n_idx);
+  if (st != FP4KV_OK) return st;
+  if (!pool_out || !n_pool) return fail(FP4KV_ERR_NULL, "index_full: pool_out and n_pool must be non-NULL");
+  if (max_ctx < 1) return fail(FP4KV_ERR_SHAPE, "index_full: max_ctx=%lld must be >= 1", (long long)max_ctx);
+  if (n_q == 0) return ok();
+  const size_t need = fp4kv_index_workspace_bytes(n_q, max_ctx, block);
+  if (!workspace || ws_bytes < need)
+    return fail(FP4KV_ERR_WORKSPACE, "index_full: workspace of %zu bytes, %zu required", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* scores = static_cast<float*>(workspace);
+  float* blockmax = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)n_q * max_ctx * sizeof(float)));
+
+  fp4kv::ScanArgs sa{};
+  sa.idx_q = static_cast<const uint16_t*>(idx_q);
+  sa.w = w;
+  sa.idx_k = static_cast<const uint16_t*>(idx_k);
+  sa.total_rows = total_rows;
+  sa.seq_start = seq_start;
+  sa.q_pos = q_pos;
+  sa.q_per_seq = q_per_seq;
+  sa.max_ctx = max_ctx;
+  sa.scores = scores;
+  sa.blockmax = blockmax;
+  sa.nblk_max = nblk_of(max_ctx, block);
+  hipError_t e = fp4kv::launch_scan(sa, H, D, n_q, max_ctx, false, s);
+  if (e != hipSuccess) return hip_status(e, "index_full scan");
+
+  fp4kv::SelectArgs se{};
+  se.seq_start = seq_start;
+  se.q_pos = q_pos;
+  se.q_per_seq = q_per_seq;
+  se.total_rows = total_rows;
+  se.max_ctx = max_ctx;
+  se.scores = scores;
+  se.blockmax = blockmax;
+  se.nblk_max = sa.nblk_max;
+  se.P = P;
+  se.k = k;
+  se.pool = pool_out;
+  se.n_pool = n_pool;
+  se.idx_out = idx_out;
+  se.n_idx = n_idx;
+  return hip_status(fp4kv::launch_select(se, n_q, false, s), "index_full select");
+}
+
+fp4kv_status fp4kv_index_reindex(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
+                                 const int64_t* seq_start, const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                                 int32_t H, int32_t D, const int32_t* pool, const int32_t* n_pool, int32_t block,
+                                 int32_t P, int32_t k, int32_t* idx_out, int32_t* n_idx, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  fp4kv_status st = check_indexer_common("index_reindex", idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q,
+                                         q_per_seq, H, D, block, P, k, idx_out, n_idx);
+  if (st != FP4KV_OK) return st;
+  if (!pool || !n_pool) return fail(FP4KV_ERR_NULL, "index_reindex: pool and n_pool must be non-NULL");
+  if (n_q == 0) return ok();
+  const size_t need = fp4kv_reindex_workspace_bytes(n_q, P, block);
+  if (!workspace || ws_bytes < need)
+    return fail(FP4KV_ERR_WORKSPACE, "index_reindex: workspace of %zu bytes, %zu required", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* pscores = static_cast<float*>(workspace);
+  // Positions are bounded by the sequence (rows past total_rows are invisible),
+  // so the clamp of q_pos uses the largest representable context.
+  const int64_t max_ctx = total_rows > 0 ? total_rows : 1;
+
+  fp4kv::ScanArgs sa{};
+  sa.idx_q = static_cast<const uint16_t*>(idx_q);
+  sa.w = w;
+  sa.idx_k = static_cast<const uint16_t*>(idx_k);
+  sa.total_rows = total_rows;
+  sa.seq_start = seq_start;
+  sa.q_pos = q_pos;
+  sa.q_per_seq = q_per_seq;
+  sa.max_ctx = max_ctx;
+  sa.pool = pool;
+  sa.n_pool = n_pool;
+  sa.P = P;
+  sa.pool_scores = pscores;
+  hipError_t e = fp4kv::launch_scan(sa, H, D, n_q, (int64_t)P * block, true, s);
+  if (e != hipSuccess) return hip_status(e, "index_reindex scan");
+
+  fp4kv::SelectArgs se{};
+  se.seq_start = seq_start;
+  se.q_pos = q_pos;
+  se.q_per_seq = q_per_seq;
+  se.total_rows = total_rows;
+  se.max_ctx = max_ctx;
+  se.scores = pscores;
+  se.P = P;
+  se.k = k;
+  se.pool = const_cast<int32_t*>(pool);
+  se.n_pool = const_cast<int32_t*>(n_pool);
+  se.idx_out = idx_out;
+  se.n_idx = n_idx;
+  return hip_status(fp4kv::launch_select(se, n_q, true, s), "index_reindex select");
+}
+
+static fp4kv_status check_attn(const char* fn, const void* q, const uint8_t* codes, const uint8_t* scales,
+                               const int32_t* idx, const int32_t* n_idx, const void* swa_k, const void* swa_v,
+                               int32_t nq, int32_t Hq, int32_t C, int32_t k, int32_t W, float scale, const float* out,
+                               void* workspace, size_t ws_bytes) {
+  if (!q || !codes || !scales || !idx || !n_idx || !swa_k || !swa_v || !out)
+    return fail(FP4KV_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (nq < 0 || Hq <= 0 || C <= 0 || k < 1 || W < 1 || k > 16384 || W > 16384)
+    return fail(FP4KV_ERR_SHAPE, "%s: n_q=%d Hq=%d C=%d k=%d W=%d out of range", fn, nq, Hq, C, k, W);
+  if (!(Hq == 16 || Hq == 32 || Hq == 64)) return fail(FP4KV_ERR_UNSUPPORTED, "%s: Hq=%d (16, 32 or 64 implemented)", fn, Hq);
+  if (C != 512) return fail(FP4KV_ERR_UNSUPPORTED, "%s: C=%d (only 512 implemented)", fn, C);
+  if (!std::isfinite(scale)) return fail(FP4KV_ERR_SHAPE, "%s: scale must be finite", fn);
+  if (!aligned16(q) || !aligned16(swa_k) || !aligned16(swa_v) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(codes) & 7u))
+    return fail(FP4KV_ERR_SHAPE, "%s: q, swa_k, swa_v, out must be 16-byte and codes 8-byte aligned", fn);
+  const size_t need = fp4kv_attn_workspace_bytes(nq, Hq, C, k, W);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(FP4KV_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu required", fn, ws_bytes, need);
+  return FP4KV_OK;
+}
+
+fp4kv_status fp4kv_sparse_attn_decode(const void* q, const uint8_t* codes, const uint8_t* scales, int64_t total_rows,
+                                      const int64_t* seq_start, const int32_t* idx, const int32_t* n_idx,
+                                      const void* swa_k, const void* swa_v, const int32_t* q_pos, int32_t B,
+                                      int32_t Hq, int32_t C, int32_t k, int32_t W, float scale, float* out, float* lse,
+                                      void* workspace, size_t ws_bytes, void* stream) {
+  fp4kv_status st = check_attn("sparse_attn_decode", q, codes, scales, idx, n_idx, swa_k, swa_v, B, Hq, C, k, W,
+                               scale, out, workspace, ws_bytes);
+  if (st != FP4KV_OK) return st;
+  if (!seq_start || !q_pos) return fail(FP4KV_ERR_NULL, "sparse_attn_decode: seq_start and q_pos must be non-NULL");
+  if (B == 0) return ok();
+  fp4kv::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.codes = codes;
+  a.scales = scales;
+  a.total_rows = total_rows;
+  a.seq_start = seq_start;
+  a.idx = idx;
+  a.n_idx = n_idx;
+  a.k = k;
+  a.swa_k = static_cast<const uint16_t*>(swa_k);
+  a.swa_v = static_cast<const uint16_t*>(swa_v);
+  a.q_pos = q_pos;
+  a.win_stride = W;
+  a.W = W;
+  a.nq = B;
+  a.Hq = Hq;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(fp4kv::launch_attn(a, workspace, static_cast<hipStream_t>(stream)), "sparse_attn_decode");
+}
+
+fp4kv_status fp4kv_sparse_attn_prefill(const void* q, const uint8_t* codes, const uint8_t* scales, int64_t total_rows,
+                                       int64_t seq_start, const int32_t* idx, const int32_t* n_idx, const void* swa_k,
+                                       const void* swa_v, int32_t pos0, int32_t T, int32_t Hq, int32_t C, int32_t k,
+                                       int32_t W, float scale, float* out, float* lse, void* workspace,
+                                       size_t ws_bytes, void* stream) {
+  fp4kv_status st = check_attn("sparse_attn_prefill", q, codes, scales, idx, n_idx, swa_k, swa_v, T, Hq, C, k, W,
+                               scale, out, workspace, ws_bytes);
+  if (st != FP4KV_OK) return st;
+  if (pos0 < 0 || seq_start < 0) return fail(FP4KV_ERR_SHAPE, "sparse_attn_prefill: pos0 and seq_start must be >= 0");
+  if (T == 0) return ok();
+  fp4kv::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.codes = codes;
+  a.scales = scales;
+  a.total_rows = total_rows;
+  a.seq_start = nullptr;
+  a.seq_start_scalar = seq_start;
+  a.idx = idx;
+  a.n_idx = n_idx;
+  a.k = k;
+  a.swa_k = static_cast<const uint16_t*>(swa_k);
+  a.swa_v = static_cast<const uint16_t*>(swa_v);
+  a.q_pos = nullptr;
+  a.pos0 = pos0;
+  a.win_stride = 1;
+  a.W = W;
+  a.nq = T;
+  a.Hq = Hq;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(fp4kv::launch_attn(a, workspace, static_cast<hipStream_t>(stream)), "sparse_attn_prefill");
+}
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// Internal helpers shared by the fp4kv kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4kv {
+
+constexpr int kWave = 64;
+
+// bfloat16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// Order-preserving map of fp32 onto uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Value of an E4M3FN code (bias 7, no infinities; 0x7F / 0xFF are NaN and never produced here).
+__host__ __device__ constexpr float e4m3_value(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag = e == 0 ? (float)m * (1.0f / 512.0f)
+                     : (float)(8u + m) * (1.0f / 8.0f) * (e >= 7 ? (float)(1u << (e - 7)) : 1.0f / (float)(1u << (7 - e)));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+}  // namespace fp4kv

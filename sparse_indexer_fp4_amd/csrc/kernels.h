@@ -1,0 +1,80 @@
+// Internal interface between the C ABI (api.hip) and the kernels: argument
+// blocks and launchers. Not part of the public header.
+#pragma once
+#include "common.h"
+
+namespace fp4kv {
+
+struct ScanArgs {
+  const uint16_t* idx_q;     // [n_q, H, D] bf16
+  const float* w;            // [n_q, H]
+  const uint16_t* idx_k;     // [total_rows, D] bf16
+  int64_t total_rows;
+  const int64_t* seq_start;  // [n_seq]
+  const int32_t* q_pos;      // [n_q]
+  int32_t q_per_seq;
+  int64_t max_ctx;
+  // Full scan outputs
+  float* scores;             // [n_q, max_ctx]
+  float* blockmax;           // [n_q, nblk_max]
+  int64_t nblk_max;
+  // Reindex scan inputs/outputs
+  const int32_t* pool;       // [n_q, P]
+  const int32_t* n_pool;     // [n_q]
+  int32_t P;
+  float* pool_scores;        // [n_q, P*8]
+  int32_t steps;             // 64-token steps per workgroup
+};
+
+struct SelectArgs {
+  const int64_t* seq_start;
+  const int32_t* q_pos;
+  int32_t q_per_seq;
+  int64_t total_rows;
+  int64_t max_ctx;
+  const float* scores;       // Full: [n_q, max_ctx]; Reindex: [n_q, P*8]
+  const float* blockmax;     // [n_q, nblk_max] (Full)
+  int64_t nblk_max;
+  int32_t P, k;
+  int32_t* pool;             // Full: output [n_q, P]; Reindex: input
+  int32_t* n_pool;           // Full: output; Reindex: input
+  int32_t* idx_out;          // [n_q, k]
+  int32_t* n_idx;            // [n_q]
+};
+
+struct AttnArgs {
+  const uint16_t* q;              // [nq, Hq, C] bf16
+  const uint8_t* codes;           // [total_rows, C/2]
+  const uint8_t* scales;          // [total_rows, C/16]
+  int64_t total_rows;
+  const int64_t* seq_start;       // [nq] (decode) or nullptr (prefill: seq_start_scalar)
+  int64_t seq_start_scalar;
+  const int32_t* idx;             // [nq, k]
+  const int32_t* n_idx;           // [nq]
+  int32_t k;
+  const uint16_t* swa_k;          // window keys, bf16
+  const uint16_t* swa_v;          // window values, bf16
+  const int32_t* q_pos;           // [nq] (decode) or nullptr (prefill: pos0 + i)
+  int32_t pos0;
+  int64_t win_stride;             // window-buffer rows between consecutive queries
+  int32_t W;
+  int32_t nq, Hq;
+  float scale_log2;               // softmax scale * log2(e)
+  int32_t n_split;
+  float* out;                     // [nq, Hq, C]
+  float* lse;                     // [nq, Hq] or nullptr
+  float* part_o;                  // [nq, n_split, Hq, C]
+  float* part_ml;                 // [nq, n_split, Hq, 2]
+};
+
+hipError_t launch_quantize_append(const void* src, int64_t n_rows, int32_t C, const int64_t* dst_rows,
+                                  int64_t dst_start, uint8_t* codes, uint8_t* scales, int64_t cap_rows,
+                                  hipStream_t stream);
+bool scan_supported(int H, int D);
+// slots: max_ctx for a Full scan, P*8 for a Reindex scan.
+hipError_t launch_scan(ScanArgs a, int H, int D, int n_q, int64_t slots, bool reindex, hipStream_t stream);
+hipError_t launch_select(const SelectArgs& a, int n_q, bool reindex, hipStream_t stream);
+size_t attn_workspace_bytes(int nq, int Hq, int k, int W);
+hipError_t launch_attn(AttnArgs a, void* ws, hipStream_t stream);
+
+}  // namespace fp4kv

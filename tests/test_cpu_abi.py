@@ -1,0 +1,66 @@
+"""The C-ABI library loads and exports every entry point include/fp4kv.h
+declares; host-side argument checks and workspace sizing work without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4kv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4kv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import sparse_indexer_fp4_amd as fk
+    return fk
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib.lib, n), n
+    assert sorted(lib.EXPORTS) == names
+
+
+def test_abi_version(lib):
+    assert lib.abi_version() == 1
+
+
+def test_null_and_shape_errors_without_gpu(lib):
+    L = lib.lib
+    assert L.fp4kv_quantize_append(None, 4, 512, None, 0, None, None, 4, None) == -1
+    assert b"non-NULL" in L.fp4kv_last_error()
+    fake = ctypes.c_void_p(4096)   # never dereferenced: the call fails validation first
+    assert L.fp4kv_quantize_append(fake, 4, 500, None, 0, fake, fake, 4, None) == -2
+    assert L.fp4kv_quantize_append(fake, 4, 512, None, 1, fake, fake, 4, None) == -2
+    assert L.fp4kv_quantize_append(fake, 0, 512, None, 0, fake, fake, 4, None) == 0
+    assert L.fp4kv_last_error() == b""
+    # index_full: block must be 8, P*block <= 16384, k <= P*block, workspace large enough
+    args = [fake, fake, fake, 100, fake, fake, 1, 1, 16, 128, 100]
+    out = [fake, fake, fake, fake]
+    assert L.fp4kv_index_full(*args, 16, 4, 2, *out, fake, 1 << 30, None) == -4
+    assert L.fp4kv_index_full(*args, 8, 4096, 2, *out, fake, 1 << 30, None) == -4
+    assert L.fp4kv_index_full(*args, 8, 4, 33, *out, fake, 1 << 30, None) == -2
+    assert L.fp4kv_index_full(*args, 8, 4, 2, *out, fake, 10, None) == -3
+    assert L.fp4kv_index_full(*[fake, fake, fake, 100, fake, fake, 1, 1, 3, 128, 100], 8, 4, 2, *out, fake,
+                              1 << 30, None) == -4
+    # attention: only C = 512 and Hq in {16, 32, 64}
+    a = [fake, fake, fake, 100, fake, fake, fake, fake, fake, fake, 1]
+    assert L.fp4kv_sparse_attn_decode(*a, 64, 256, 8, 128, ctypes.c_float(0.1), fake, None, fake, 1 << 30, None) == -4
+    assert L.fp4kv_sparse_attn_decode(*a, 48, 512, 8, 128, ctypes.c_float(0.1), fake, None, fake, 1 << 30, None) == -4
+    assert L.fp4kv_sparse_attn_decode(*a, 64, 512, 0, 128, ctypes.c_float(0.1), fake, None, fake, 1 << 30, None) == -2
+
+
+def test_workspace_sizes(lib):
+    assert lib.fp4kv_index_workspace_bytes(32, 131072) >= 32 * 131072 * 4 + 32 * 16384 * 4
+    assert lib.fp4kv_reindex_workspace_bytes(8, 2048) >= 8 * 2048 * 8 * 4
+    assert lib.fp4kv_attn_workspace_bytes(4096, 64, 512, 512, 128) == 0   # one split when queries fill the GPU
+    assert lib.fp4kv_attn_workspace_bytes(1, 64, 512, 512, 128) > 0
