@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the Full-layer decode step at 128K context on one MI355X.
+
+Workload (decode128k): 32 queries, each with its own 131,072-token context;
+indexer 16 heads x 128 dims (integers in [-8, 8] as bf16, weights in [1, 8]);
+pool of the best 2,048 blocks of 8 tokens, top 512 tokens; attention with 64
+heads over the 512-channel FP4 main-KV latent plus a 128-token bf16 window.
+Inputs are synthetic, seeded, generated on the GPU, resident in HBM before
+timing starts.
+
+One step = the whole hot path of the layer for the batch:
+  fp4kv_quantize_append   (the newest token's KV row of each sequence)
+  fp4kv_index_scores      (indexer scan + 8-token block max)
+  fp4kv_index_select      (top-2,048 blocks -> pool -> top-512 tokens)
+  fp4kv_sparse_attn_decode (FP4 gather-dequant attention + window + LSE merge)
+
+Prints one JSON line (see the README of the contract in the design doc).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode queries/s + HBM GB/s (% of peak), Full-layer sparse attn @128K ctx"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg):
+    """Compulsory HBM bytes per call, counting inputs once and outputs once."""
+    B, N = cfg.n_seq, cfg.ctx
+    nblk = (N + 7) // 8
+    scan = (B * N * cfg.D * 2            # indexer keys
+            + B * cfg.H * cfg.D * 2      # indexer queries
+            + B * cfg.H * 4              # head weights
+            + B * N * 4 + B * nblk * 4)  # token scores + block maxima written
+    select = (B * nblk * 4                       # block maxima read
+              + B * cfg.P * 8 * 4                # pool token scores read
+              + B * (cfg.P + cfg.k + 2) * 4)     # pool, indices, counts written
+    row = cfg.C // 2 + cfg.C // 16               # 288 B per FP4 row
+    attn = B * (cfg.k * row                      # gathered FP4 rows
+                + cfg.k * 4                      # indices
+                + cfg.Hq * cfg.C * 2             # main Q
+                + 2 * cfg.W * cfg.C * 2          # window K and V
+                + cfg.Hq * cfg.C * 4 + cfg.Hq * 4)   # output and lse
+    append = B * (cfg.C * 2 + row + 8)           # bf16 row in, FP4 row + destination out
+    # The layer as the pages' path defines it: every input once, every final output once.
+    layer = (B * N * cfg.D * 2 + B * cfg.H * cfg.D * 2 + B * cfg.H * 4
+             + B * (cfg.P + cfg.k) * 4 + attn - B * cfg.k * 4 + append)
+    return {"scan": scan, "select": select, "attn": attn, "append": append, "layer": layer}
+
+
+def cpu_baseline(cfg, n_sample):
+    """The oracle, as it stands, on n_sample queries of the same workload:
+    Full-layer indexer + attention per query. Input generation is not timed."""
+    import numpy as np
+    import torch
+    from synth import bf16_to_f64
+    from synth import workloads as wl
+    from tests import oracle_runner as orun
+    from oracle import attention, fp4, indexer
+
+    torch.set_num_threads(os.cpu_count() or 1)
+    prepared = []
+    for i in range(n_sample):
+        s = wl.sequence_of(cfg, i)
+        p = int(cfg.q_pos()[i])
+        krows = orun.host_idx_k(cfg, s, p + 1)
+        q, w = wl.indexer_query(cfg, 0, i)
+        Q = bf16_to_f64(wl.main_query(cfg, 0, i))
+        wpos = torch.arange(max(0, p - cfg.W + 1), p + 1, dtype=torch.int64)
+        wk = bf16_to_f64(wl.window_rows(cfg, 0, s, wpos, "k"))
+        wv = bf16_to_f64(wl.window_rows(cfg, 0, s, wpos, "v"))
+        prepared.append((s, p, krows, bf16_to_f64(q), w.numpy().astype(np.float64), Q, wk, wv))
+    # bf16 rows of every position a query may select are regenerated inside the
+    # timed region only as the oracle's codec input; their generation is timed
+    # separately and subtracted.
+    t_gen = 0.0
+    t0 = time.perf_counter()
+    for (s, p, krows, q, w, Q, wk, wv) in prepared:
+        pool, idx, _ = indexer.index_full(q, w, krows, p, cfg.P, cfg.k)
+        tg = time.perf_counter()
+        x = bf16_to_f64(wl.kv_rows(cfg, s, torch.from_numpy(idx)))
+        t_gen += time.perf_counter() - tg
+        rows = fp4.dequantize_rows(*fp4.quantize_rows(x))
+        attention.attend(Q, rows, wk, wv, cfg.scale)
+    dt = time.perf_counter() - t0 - t_gen
+    threads = torch.get_num_threads()
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [threads])
+    except Exception:
+        pass
+    return {"value": n_sample / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_sample} of the 32 queries of decode128k (Full-layer indexer + attention per query, "
+                      f"float64 numpy; {dt:.1f} s; input generation excluded)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-sample", type=int, default=32, help="queries timed on the oracle (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the decode batch shards by query "
+              f"with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_indexer_fp4_amd as fk
+    from synth import workloads as wl
+    from tests.gpu_inputs import DeviceWorkload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = wl.CONFIGS["decode128k"]
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    log(f"generating {cfg.name} inputs on the GPU")
+    dw = DeviceWorkload(cfg, dev)
+    new_x, new_dst = dw.newest_rows()
+    B, N = cfg.n_seq, cfg.ctx
+    nblk = (N + 7) // 8
+    scores = torch.empty((B, N), dtype=torch.float32, device=dev)
+    blockmax = torch.empty((B, nblk), dtype=torch.float32, device=dev)
+    pool = torch.empty((B, cfg.P), dtype=torch.int32, device=dev)
+    n_pool = torch.empty((B,), dtype=torch.int32, device=dev)
+    idx = torch.empty((B, cfg.k), dtype=torch.int32, device=dev)
+    n_idx = torch.empty((B,), dtype=torch.int32, device=dev)
+    out = torch.empty((B, cfg.Hq, cfg.C), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, cfg.Hq), dtype=torch.float32, device=dev)
+    aws = torch.empty(max(1, fk.fp4kv_attn_workspace_bytes(B, cfg.Hq, cfg.C, cfg.k, cfg.W)), dtype=torch.uint8,
+                      device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fk.fp4kv_quantize_append(new_x, dw.codes, dw.scales, dst_rows=new_dst, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fk.fp4kv_index_scores(dw.idx_q[0], dw.w[0], dw.idx_k, dw.seq_start, dw.q_pos, 1, N, scores=scores,
+                              blockmax=blockmax, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fk.fp4kv_index_select(scores, blockmax, dw.total_rows, dw.seq_start, dw.q_pos, 1, cfg.P, cfg.k,
+                              pool_out=pool, n_pool=n_pool, idx_out=idx, n_idx=n_idx, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        fk.fp4kv_sparse_attn_decode(dw.q[0], dw.codes, dw.scales, dw.seq_start, idx, n_idx, dw.swa_k[0],
+                                    dw.swa_v[0], dw.q_pos, cfg.scale, out=out, lse=lse, workspace=aws, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    per = {"append": 0.0, "scan": 0.0, "select": 0.0, "attn": 0.0}
+    for ev in evs:
+        per["append"] += ev[0].elapsed_time(ev[1])
+        per["scan"] += ev[1].elapsed_time(ev[2])
+        per["select"] += ev[2].elapsed_time(ev[3])
+        per["attn"] += ev[3].elapsed_time(ev[4])
+    per = {k: v / args.steps for k, v in per.items()}          # ms per launch
+    ms_step = 1e3 * elapsed / args.steps
+    nbytes = algorithmic_bytes(cfg)
+    scan_gbps = nbytes["scan"] / (per["scan"] * 1e-3) / 1e9
+    layer_gbps = nbytes["layer"] / (ms_step * 1e-3) / 1e9
+
+    rec = {
+        "metric": METRIC,
+        "value": B / (ms_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode128k: Full-layer decode step, 32 queries x 131,072-token contexts, "
+                               "indexer 16x128, pool 2,048 blocks of 8, top-512, 64 heads x 512-channel FP4 latent, "
+                               "128-token bf16 window",
+                   "batch": B, "ctx": N, "pool_blocks": cfg.P, "top_k": cfg.k, "heads": cfg.Hq,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "indexer scan (fp4kv_index_scores)",
+                     "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": scan_gbps / HBM_PEAK_GBPS, "traffic": None},
+        "detail": {"ms_per_launch": per, "algorithmic_bytes": nbytes,
+                   "layer_hbm_gbps": layer_gbps, "layer_frac_of_peak": layer_gbps / HBM_PEAK_GBPS},
+    }
+    if args.cpu_sample > 0:
+        log(f"timing the oracle on {args.cpu_sample} queries")
+        rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
+    else:
+        rec["cpu_baseline"] = None
+    log(f"done in {time.perf_counter() - t0:.1f} s")
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -150,6 +150,34 @@ fp4kv_status fp4kv_index_full(const void* idx_q, const float* w, const void* idx
                               int32_t* idx_out, int32_t* n_idx, void* workspace,
                               size_t ws_bytes, void* stream);
 
+/*
+ * The two halves of fp4kv_index_full, for callers that keep the scores:
+ *
+ * fp4kv_index_scores: token scores and block maxima of every visible token
+ * (the scan). Same arguments and scoring rule as fp4kv_index_full; writes
+ *   scores    (device) fp32 [n_q, max_ctx]: score of position t of query i at
+ *             scores[i*max_ctx + t] for t <= the clamped q_pos[i] (rows past
+ *             total_rows excluded); other entries are left untouched;
+ *   blockmax  (device) fp32 [n_q, ceil(max_ctx/block)]: max over the visible
+ *             tokens of each block with at least one visible token.
+ *
+ * fp4kv_index_select: the candidate pool and the top-k positions from those
+ * buffers (same ranking and outputs as fp4kv_index_full). seq_start, q_pos,
+ * total_rows, q_per_seq, max_ctx and block must be the values the scores were
+ * computed with.
+ */
+fp4kv_status fp4kv_index_scores(const void* idx_q, const float* w, const void* idx_k,
+                                int64_t total_rows, const int64_t* seq_start,
+                                const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                                int32_t H, int32_t D, int64_t max_ctx, int32_t block,
+                                float* scores, float* blockmax, void* stream);
+
+fp4kv_status fp4kv_index_select(const float* scores, const float* blockmax, int64_t total_rows,
+                                const int64_t* seq_start, const int32_t* q_pos, int32_t n_q,
+                                int32_t q_per_seq, int64_t max_ctx, int32_t block, int32_t P,
+                                int32_t k, int32_t* pool_out, int32_t* n_pool, int32_t* idx_out,
+                                int32_t* n_idx, void* stream);
+
 /* Workspace bytes fp4kv_index_reindex needs (pool token scores, fp32). */
 size_t fp4kv_reindex_workspace_bytes(int32_t n_q, int32_t P, int32_t block);
 

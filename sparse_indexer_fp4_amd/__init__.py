@@ -4,7 +4,7 @@ Every function takes torch tensors on the GPU, passes their device pointers and
 the current HIP stream to the C ABI, and raises Fp4kvError on a negative
 status. Nothing here computes any part of the method; all of it runs in the
 HIP kernels of libfp4kv.so. The library must have been built
-(python -m sparse_indexer_fp4_amd.build); importing this package without it
+(python sparse_indexer_fp4_amd/build.py); importing this package without it
 raises.
 """
 from __future__ import annotations
@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp4kv.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_indexer_fp4_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_indexer_fp4_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -35,6 +35,8 @@ _SIGS = {
     "fp4kv_index_workspace_bytes": (_sz, [_i32, _i64, _i32]),
     "fp4kv_index_full": (_i32, [_p, _p, _p, _i64, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
                                 _p, _p, _p, _p, _p, _sz, _p]),
+    "fp4kv_index_scores": (_i32, [_p, _p, _p, _i64, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _p, _p, _p]),
+    "fp4kv_index_select": (_i32, [_p, _p, _i64, _p, _p, _i32, _i32, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]),
     "fp4kv_reindex_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "fp4kv_index_reindex": (_i32, [_p, _p, _p, _i64, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _i32, _i32, _i32,
                                    _p, _p, _p, _sz, _p]),
@@ -132,6 +134,37 @@ def fp4kv_index_full(idx_q, w, idx_k, seq_start, q_pos, q_per_seq, max_ctx, P, k
     _check(lib.fp4kv_index_full(_ptr(idx_q), _ptr(w), _ptr(idx_k), idx_k.shape[0], _ptr(seq_start), _ptr(q_pos),
                                 n_q, q_per_seq, H, D, max_ctx, block, P, k, _ptr(pool_out), _ptr(n_pool),
                                 _ptr(idx_out), _ptr(n_idx), _ptr(ws), ws.numel(), _stream(stream)))
+    return pool_out, n_pool, idx_out, n_idx
+
+
+def fp4kv_index_scores(idx_q, w, idx_k, seq_start, q_pos, q_per_seq, max_ctx, block=8, scores=None, blockmax=None,
+                       stream=None):
+    """Scan half of the Full indexer. Returns (scores f32 [n_q, max_ctx], blockmax f32 [n_q, nblk])."""
+    _expect(idx_q, torch.bfloat16, "idx_q"); _expect(w, torch.float32, "w"); _expect(idx_k, torch.bfloat16, "idx_k")
+    n_q, H, D = idx_q.shape
+    dev = idx_q.device
+    nblk = (max_ctx + block - 1) // block
+    scores = torch.empty((n_q, max_ctx), dtype=torch.float32, device=dev) if scores is None else scores
+    blockmax = torch.empty((n_q, nblk), dtype=torch.float32, device=dev) if blockmax is None else blockmax
+    _check(lib.fp4kv_index_scores(_ptr(idx_q), _ptr(w), _ptr(idx_k), idx_k.shape[0], _ptr(seq_start), _ptr(q_pos),
+                                  n_q, q_per_seq, H, D, max_ctx, block, _ptr(scores), _ptr(blockmax),
+                                  _stream(stream)))
+    return scores, blockmax
+
+
+def fp4kv_index_select(scores, blockmax, total_rows, seq_start, q_pos, q_per_seq, P, k, block=8, pool_out=None,
+                       n_pool=None, idx_out=None, n_idx=None, stream=None):
+    """Selection half of the Full indexer. Returns (pool, n_pool, idx, n_idx)."""
+    _expect(scores, torch.float32, "scores"); _expect(blockmax, torch.float32, "blockmax")
+    n_q, max_ctx = scores.shape
+    dev = scores.device
+    pool_out = torch.empty((n_q, P), dtype=torch.int32, device=dev) if pool_out is None else pool_out
+    n_pool = torch.empty((n_q,), dtype=torch.int32, device=dev) if n_pool is None else n_pool
+    idx_out = torch.empty((n_q, k), dtype=torch.int32, device=dev) if idx_out is None else idx_out
+    n_idx = torch.empty((n_q,), dtype=torch.int32, device=dev) if n_idx is None else n_idx
+    _check(lib.fp4kv_index_select(_ptr(scores), _ptr(blockmax), int(total_rows), _ptr(seq_start), _ptr(q_pos), n_q,
+                                  q_per_seq, max_ctx, block, P, k, _ptr(pool_out), _ptr(n_pool), _ptr(idx_out),
+                                  _ptr(n_idx), _stream(stream)))
     return pool_out, n_pool, idx_out, n_idx
 
 

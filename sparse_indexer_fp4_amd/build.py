@@ -1,6 +1,6 @@
 """Build libfp4kv.so (gfx950) in-tree from csrc/*.hip with hipcc.
 
-    python -m sparse_indexer_fp4_amd.build
+    python sparse_indexer_fp4_amd/build.py
 
 Objects go to _build/ at the repository root; the library goes next to this file.
 """

@@ -99,6 +99,48 @@ static fp4kv_status check_indexer_common(const char* fn, const void* idx_q, cons
   return FP4KV_OK;
 }
 
+static fp4kv_status launch_scores(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
+                                  const int64_t* seq_start, const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                                  int32_t H, int32_t D, int64_t max_ctx, int32_t block, float* scores,
+                                  float* blockmax, hipStream_t s) {
+  fp4kv::ScanArgs sa{};
+  sa.idx_q = static_cast<const uint16_t*>(idx_q);
+  sa.w = w;
+  sa.idx_k = static_cast<const uint16_t*>(idx_k);
+  sa.total_rows = total_rows;
+  sa.seq_start = seq_start;
+  sa.q_pos = q_pos;
+  sa.q_per_seq = q_per_seq;
+  sa.max_ctx = max_ctx;
+  sa.scores = scores;
+  sa.blockmax = blockmax;
+  sa.nblk_max = nblk_of(max_ctx, block);
+  return hip_status(fp4kv::launch_scan(sa, H, D, n_q, max_ctx, false, s), "index scan");
+}
+
+static fp4kv_status launch_select_full(const float* scores, const float* blockmax, int64_t total_rows,
+                                       const int64_t* seq_start, const int32_t* q_pos, int32_t n_q,
+                                       int32_t q_per_seq, int64_t max_ctx, int32_t block, int32_t P, int32_t k,
+                                       int32_t* pool_out, int32_t* n_pool, int32_t* idx_out, int32_t* n_idx,
+                                       hipStream_t s) {
+  fp4kv::SelectArgs se{};
+  se.seq_start = seq_start;
+  se.q_pos = q_pos;
+  se.q_per_seq = q_per_seq;
+  se.total_rows = total_rows;
+  se.max_ctx = max_ctx;
+  se.scores = scores;
+  se.blockmax = blockmax;
+  se.nblk_max = nblk_of(max_ctx, block);
+  se.P = P;
+  se.k = k;
+  se.pool = pool_out;
+  se.n_pool = n_pool;
+  se.idx_out = idx_out;
+  se.n_idx = n_idx;
+  return hip_status(fp4kv::launch_select(se, n_q, false, s), "index select");
+}
+
 fp4kv_status fp4kv_index_full(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
                               const int64_t* seq_start, const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
                               int32_t H, int32_t D, int64_t max_ctx, int32_t block, int32_t P, int32_t k,
@@ -116,38 +158,43 @@ fp4kv_status fp4kv_index_full(const void* idx_q, const float* w, const void* idx
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* scores = static_cast<float*>(workspace);
   float* blockmax = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)n_q * max_ctx * sizeof(float)));
+  st = launch_scores(idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D, max_ctx, block, scores,
+                     blockmax, s);
+  if (st != FP4KV_OK) return st;
+  return launch_select_full(scores, blockmax, total_rows, seq_start, q_pos, n_q, q_per_seq, max_ctx, block, P, k,
+                            pool_out, n_pool, idx_out, n_idx, s);
+}
 
-  fp4kv::ScanArgs sa{};
-  sa.idx_q = static_cast<const uint16_t*>(idx_q);
-  sa.w = w;
-  sa.idx_k = static_cast<const uint16_t*>(idx_k);
-  sa.total_rows = total_rows;
-  sa.seq_start = seq_start;
-  sa.q_pos = q_pos;
-  sa.q_per_seq = q_per_seq;
-  sa.max_ctx = max_ctx;
-  sa.scores = scores;
-  sa.blockmax = blockmax;
-  sa.nblk_max = nblk_of(max_ctx, block);
-  hipError_t e = fp4kv::launch_scan(sa, H, D, n_q, max_ctx, false, s);
-  if (e != hipSuccess) return hip_status(e, "index_full scan");
+fp4kv_status fp4kv_index_scores(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
+                                const int64_t* seq_start, const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                                int32_t H, int32_t D, int64_t max_ctx, int32_t block, float* scores,
+                                float* blockmax, void* stream) {
+  int32_t dummy = 0;
+  fp4kv_status st = check_indexer_common("index_scores", idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q,
+                                         q_per_seq, H, D, block, 1, 1, &dummy, &dummy);
+  if (st != FP4KV_OK) return st;
+  if (!scores || !blockmax) return fail(FP4KV_ERR_NULL, "index_scores: scores and blockmax must be non-NULL");
+  if (max_ctx < 1) return fail(FP4KV_ERR_SHAPE, "index_scores: max_ctx=%lld must be >= 1", (long long)max_ctx);
+  if (n_q == 0) return ok();
+  return launch_scores(idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D, max_ctx, block, scores,
+                       blockmax, static_cast<hipStream_t>(stream));
+}
 
-  fp4kv::SelectArgs se{};
-  se.seq_start = seq_start;
-  se.q_pos = q_pos;
-  se.q_per_seq = q_per_seq;
-  se.total_rows = total_rows;
-  se.max_ctx = max_ctx;
-  se.scores = scores;
-  se.blockmax = blockmax;
-  se.nblk_max = sa.nblk_max;
-  se.P = P;
-  se.k = k;
-  se.pool = pool_out;
-  se.n_pool = n_pool;
-  se.idx_out = idx_out;
-  se.n_idx = n_idx;
-  return hip_status(fp4kv::launch_select(se, n_q, false, s), "index_full select");
+fp4kv_status fp4kv_index_select(const float* scores, const float* blockmax, int64_t total_rows,
+                                const int64_t* seq_start, const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                                int64_t max_ctx, int32_t block, int32_t P, int32_t k, int32_t* pool_out,
+                                int32_t* n_pool, int32_t* idx_out, int32_t* n_idx, void* stream) {
+  if (!scores || !blockmax || !seq_start || !q_pos || !pool_out || !n_pool || !idx_out || !n_idx)
+    return fail(FP4KV_ERR_NULL, "index_select: a required pointer is NULL");
+  if (n_q < 0 || q_per_seq < 1 || total_rows < 0 || max_ctx < 1)
+    return fail(FP4KV_ERR_SHAPE, "index_select: n_q >= 0, q_per_seq >= 1, total_rows >= 0, max_ctx >= 1 required");
+  if (block != 8) return fail(FP4KV_ERR_UNSUPPORTED, "index_select: block=%d (only 8 is implemented)", block);
+  if (P < 1 || k < 1) return fail(FP4KV_ERR_SHAPE, "index_select: P=%d and k=%d must be >= 1", P, k);
+  if ((int64_t)P * block > 16384) return fail(FP4KV_ERR_UNSUPPORTED, "index_select: P*block exceeds 16384");
+  if (k > P * block) return fail(FP4KV_ERR_SHAPE, "index_select: k=%d exceeds P*block=%d", k, P * block);
+  if (n_q == 0) return ok();
+  return launch_select_full(scores, blockmax, total_rows, seq_start, q_pos, n_q, q_per_seq, max_ctx, block, P, k,
+                            pool_out, n_pool, idx_out, n_idx, static_cast<hipStream_t>(stream));
 }
 
 fp4kv_status fp4kv_index_reindex(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
