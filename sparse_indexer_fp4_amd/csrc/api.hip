@@ -6,7 +6,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/fp4kv.h"
+#include "fp4kv.h"
 #include "kernels.h"
 
 
