@@ -8,65 +8,113 @@
 // Ranking: score descending, ties to the lower block id / position. Output:
 // ascending ids, -1 after the count.
 //
-// One 1024-thread workgroup per query. A selection of kk out of n keys is a
-// radix select on order-preserving 32-bit keys: digits of 8 bits from the most
-// significant, skipping bits all candidates share, with per-wave histograms in
-// LDS; it ends with the exact threshold key T and how many keys equal to T
-// must be taken. Then an ordered compaction: every thread owns a contiguous
-// run of keys, counts (> T) and (== T) in it, a block-wide prefix sum gives
-// each run the number of ties before it (ties go to lower indices) and its
-// output offset, and each thread writes its selected ids in index order.
-// Nothing depends on the order of atomic updates, so results are deterministic.
+// One 1024-thread workgroup per query. Scores map to order-preserving 32-bit
+// keys (0 = not a candidate). Each thread owns a contiguous run of 16 keys,
+// held in registers (a longer block list is re-read from global memory in
+// each pass instead). A selection of kk of the candidates is
+//   1. a radix search for the threshold key T: 8-bit digits from the highest
+//      bit where the candidates differ, per-wave histograms in LDS, bin totals
+//      summed by 256 threads, the bin that reaches rank kk found by one wave;
+//      it stops early when that bin holds exactly the keys still needed;
+//   2. an ordered compaction: each run counts keys > T and == T; one
+//      block-wide prefix sum of both counts gives each run its output offset
+//      (the ties taken before a run are the lesser of the ties before it and
+//      the ties to take, since ties go to lower indices), and the run writes
+//      its selected ids in index order.
+// Keys bunch in a narrow range (block maxima share exponent bits), so the
+// digits start at the highest bit where candidates differ and stop at the
+// lowest: bits common to every candidate cost no pass, and the first pass
+// spreads the LDS atomics over many bins instead of one or two.
+// Nothing depends on the order of atomic updates: results are deterministic.
 #include "kernels.h"
 
 namespace fp4kv {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kSelLdsKeys = 16384;          // keys held in LDS (64 KB)
-
+constexpr int kKPT = 16;                     // keys per thread held in registers
+constexpr int kRegKeys = kSelThreads * kKPT; // 16384
 
 struct SelShared {
-  uint32_t keys[kSelLdsKeys];
   uint32_t hist[kSelWaves][256];
-  int32_t pool[kSelLdsKeys / 8];
+  uint32_t tot[256];
+  int32_t pool[kRegKeys / 8];
+  int32_t scan[kSelWaves];
+  int32_t scan2[kSelWaves][2];
   uint32_t red[kSelWaves][2];
-  int32_t scan[kSelWaves][2];
-  uint32_t bcast[4];
+  uint32_t bc[4];
 };
 
-// Block-wide exclusive prefix sums of two ints; also returns the totals.
-__device__ __forceinline__ void block_scan2(SelShared& sh, int a, int b, int& ea, int& eb, int& ta, int& tb) {
+// Exclusive prefix sum over the workgroup; also returns the total.
+__device__ __forceinline__ int block_exclusive_scan(SelShared& sh, int v, int& total) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  int ia = a, ib = b;
+  int x = v;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
-    int xa = __shfl_up(ia, d), xb = __shfl_up(ib, d);
-    if (lane >= d) { ia += xa; ib += xb; }
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
   }
-  if (lane == kWave - 1) { sh.scan[wave][0] = ia; sh.scan[wave][1] = ib; }
+  if (lane == kWave - 1) sh.scan[wave] = x;
   __syncthreads();
-  int pa = 0, pb = 0, sa = 0, sb = 0;
+  int before = 0, all = 0;
+#pragma unroll
   for (int w = 0; w < kSelWaves; ++w) {
-    int va = sh.scan[w][0], vb = sh.scan[w][1];
-    if (w < wave) { pa += va; pb += vb; }
-    sa += va; sb += vb;
+    const int s = sh.scan[w];
+    before += w < wave ? s : 0;
+    all += s;
   }
-  ea = pa + ia - a; eb = pb + ib - b; ta = sa; tb = sb;
   __syncthreads();
+  total = all;
+  return before + x - v;
 }
 
-// Threshold of a top-kk selection over n keys (key 0 = not a candidate; every
-// candidate key is nonzero). Returns T and the number of keys equal to T to take.
-template <typename KeyFn>
-__device__ void radix_threshold(SelShared& sh, KeyFn key, int64_t n, int kk, uint32_t& T, int& take_eq) {
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  // bits shared by all candidates
-  uint32_t vor = 0, vand = 0xFFFFFFFFu;
-  for (int64_t i = tid; i < n; i += kSelThreads) {
-    uint32_t v = key(i);
-    if (v) { vor |= v; vand &= v; }
+// Exclusive prefix sums of two values over the workgroup, with totals.
+__device__ __forceinline__ void block_exclusive_scan2(SelShared& sh, int a, int b, int& ea, int& eb, int& ta, int& tb) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  int x = a, y = b;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int u = __shfl_up(x, d), v = __shfl_up(y, d);
+    if (lane >= d) { x += u; y += v; }
   }
+  if (lane == kWave - 1) { sh.scan2[wave][0] = x; sh.scan2[wave][1] = y; }
+  __syncthreads();
+  int bx = 0, by = 0, sx = 0, sy = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int u = sh.scan2[w][0], v = sh.scan2[w][1];
+    if (w < wave) { bx += u; by += v; }
+    sx += u; sy += v;
+  }
+  __syncthreads();
+  ea = bx + x - a; eb = by + y - b; ta = sx; tb = sy;
+}
+
+// Keys of the calling thread's run: either 16 registers or a global-memory run.
+struct RegKeys {
+  uint32_t k[kKPT];
+  template <typename F> __device__ __forceinline__ void each(F f) const {
+#pragma unroll
+    for (int j = 0; j < kKPT; ++j) f(j, k[j]);
+  }
+};
+
+struct GlobalKeys {        // block maxima of a long context, keys computed on the fly
+  const float* bm;
+  int64_t lo, hi;          // this thread's run [lo, hi)
+  template <typename F> __device__ __forceinline__ void each(F f) const {
+    for (int64_t i = lo; i < hi; ++i) f((int)(i - lo), float_key(bm[i]));
+  }
+};
+
+// Threshold key T of a top-kk selection, and how many keys equal to T to take
+// (INT_MAX when every key equal to T is selected).
+template <typename Keys>
+__device__ void radix_threshold(SelShared& sh, const Keys& keys, int kk, uint32_t& T, int& take_eq) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  uint32_t vor = 0, vand = 0xFFFFFFFFu;
+  keys.each([&](int, uint32_t v) { if (v) { vor |= v; vand &= v; } });
+#pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
     vor |= __shfl_xor(vor, d);
     vand &= __shfl_xor(vand, d);
@@ -74,96 +122,100 @@ __device__ void radix_threshold(SelShared& sh, KeyFn key, int64_t n, int kk, uin
   if (lane == 0) { sh.red[wave][0] = vor; sh.red[wave][1] = vand; }
   __syncthreads();
   vor = 0; vand = 0xFFFFFFFFu;
+#pragma unroll
   for (int w = 0; w < kSelWaves; ++w) { vor |= sh.red[w][0]; vand &= sh.red[w][1]; }
-  __syncthreads();
   const uint32_t diff = vor ^ vand;
-  uint32_t prefix, mask;
+  if (diff == 0) { T = vand; take_eq = kk; __syncthreads(); return; }  // all candidates equal: the first kk
+  // Only bits lo..hi differ between candidates: digits of up to 8 bits cover
+  // them from the top, so the first pass already spreads over many bins.
+  const int hi = 31 - __clz(diff), lo = __builtin_ctz(diff);
+  // bits above hi: every candidate agrees (2u << 31 wraps to 0, so hi = 31 gives an empty mask)
+  uint32_t mask = ~((2u << hi) - 1u);
+  uint32_t prefix = vand & mask;
   int kr = kk;
-  if (diff == 0) {                      // all candidates equal
-    T = vand; take_eq = kk;
-    return;
-  }
-  const int top = 31 - __clz(diff);     // highest bit that differs
-  int shift = (top / 8) * 8;
-  mask = shift + 8 >= 32 ? 0u : ~((1u << (shift + 8)) - 1u);
-  prefix = vand & mask;
-  for (; shift >= 0; shift -= 8) {
+  take_eq = -1;
+  for (int top = hi; top >= lo; top -= 8) {
+    const int shift = top - 7 > lo ? top - 7 : lo;
+    const int width = top - shift + 1;
+    const uint32_t dmask = (1u << width) - 1u;
     for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&sh.hist[0][0])[i] = 0;
     __syncthreads();
-    for (int64_t i = tid; i < n; i += kSelThreads) {
-      uint32_t v = key(i);
-      if (v && (v & mask) == prefix) atomicAdd(&sh.hist[wave][(v >> shift) & 255u], 1u);
+    keys.each([&](int, uint32_t v) {
+      if (v && (v & mask) == prefix) atomicAdd(&sh.hist[wave][(v >> shift) & dmask], 1u);
+    });
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < kSelWaves; ++w) t += sh.hist[w][tid];
+      sh.tot[tid] = t;
     }
     __syncthreads();
     if (wave == 0) {
-      // lane owns bins 4*lane .. 4*lane+3; suffix sums from the top bin down
-      uint32_t c[4], s = 0;
+      // lane owns bins 4*lane .. 4*lane+3; counts from the top bin down
+      uint32_t c[4], t = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t t = 0;
-        for (int w = 0; w < kSelWaves; ++w) t += sh.hist[w][4 * lane + j];
-        c[j] = t; s += t;
-      }
-      uint32_t above = 0;  // keys in bins of higher lanes
-      uint32_t incl = s;
+      for (int j = 0; j < 4; ++j) { c[j] = sh.tot[4 * lane + j]; t += c[j]; }
+      uint32_t incl = t;
+#pragma unroll
       for (int d = 1; d < kWave; d <<= 1) {
-        uint32_t x = __shfl_down(incl, d);
+        const uint32_t x = __shfl_down(incl, d);
         if (lane + d < kWave) incl += x;
       }
-      above = incl - s;
-      // find the bin where the count from the top reaches kr
-      uint32_t run = above;
-      int found = -1; uint32_t before = 0;
+      uint32_t run = incl - t;  // keys in bins above this lane's bins
+#pragma unroll
       for (int j = 3; j >= 0; --j) {
-        if (found < 0 && run < (uint32_t)kr && run + c[j] >= (uint32_t)kr) { found = 4 * lane + j; before = run; }
+        if (run < (uint32_t)kr && run + c[j] >= (uint32_t)kr) {
+          sh.bc[0] = (uint32_t)(4 * lane + j);
+          sh.bc[1] = run;
+          sh.bc[2] = c[j];
+        }
         run += c[j];
       }
-      if (found >= 0) { sh.bcast[0] = (uint32_t)found; sh.bcast[1] = before; }
     }
     __syncthreads();
-    const uint32_t bin = sh.bcast[0];
-    kr -= (int)sh.bcast[1];
+    const uint32_t bin = sh.bc[0];
+    kr -= (int)sh.bc[1];
+    const int in_bin = (int)sh.bc[2];
     prefix |= bin << shift;
-    mask |= 255u << shift;
-    __syncthreads();
+    mask |= dmask << shift;
+    if (in_bin == kr) {           // every key left in the bin is selected
+      take_eq = 0x7FFFFFFF;
+      break;
+    }
   }
-  T = prefix;
-  take_eq = kr;
+  __syncthreads();
+  // bits below the last digit: all candidates share them (common low bits)
+  T = prefix | (vand & ~mask);
+  if (take_eq < 0) take_eq = kr;
 }
 
-// Ordered compaction: write out(slot, i) for the selected indices i in
-// increasing order. Thread t owns indices [t*per, (t+1)*per).
-template <typename KeyFn, typename OutFn>
-__device__ int compact_selected(SelShared& sh, KeyFn key, int64_t n, uint32_t T, int take_eq, OutFn out) {
-  const int tid = threadIdx.x;
-  const int64_t per = (n + kSelThreads - 1) / kSelThreads;
-  const int64_t lo = min((int64_t)tid * per, n), hi = min(lo + per, n);
+// Ordered compaction; out(slot, local index j) for selected keys of this run.
+// One scan of (count > T, count == T): the ties taken before a run are
+// min(ties before it, take_eq), because ties are taken from the lowest index.
+template <typename Keys, typename Out>
+__device__ int compact_selected(SelShared& sh, const Keys& keys, uint32_t T, int take_eq, Out out) {
   int gt = 0, eq = 0;
-  for (int64_t i = lo; i < hi; ++i) {
-    uint32_t v = key(i);
-    gt += v > T;
-    eq += (v == T) & (v != 0u);
-  }
-  int eq_before, d0, d1, d2;
-  block_scan2(sh, eq, 0, eq_before, d0, d1, d2);
+  keys.each([&](int, uint32_t v) { gt += v > T; eq += (v == T) & (v != 0u); });
+  int gt_total, eq_total;
+  int gt_before, eq_before;
+  block_exclusive_scan2(sh, gt, eq, gt_before, eq_before, gt_total, eq_total);
+  const int taken_before = min(eq_before, take_eq);
   int take = take_eq - eq_before;
   take = take < 0 ? 0 : (take > eq ? eq : take);
-  int slot, total, d3, d4;
-  block_scan2(sh, gt + take, 0, slot, d3, total, d4);
+  int slot = gt_before + taken_before;
   int taken = 0;
-  for (int64_t i = lo; i < hi; ++i) {
-    uint32_t v = key(i);
+  keys.each([&](int j, uint32_t v) {
     bool sel = v > T;
     if (!sel && v == T && v != 0u && taken < take) { sel = true; ++taken; }
-    if (sel) out(slot++, i);
-  }
-  return total;
+    if (sel) out(slot++, j);
+  });
+  return gt_total + min(eq_total, take_eq);
 }
 
 template <bool REINDEX>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  SelShared& sh = *reinterpret_cast<SelShared*>(smem);
+  __shared__ SelShared sh;
   const int qi = blockIdx.x, tid = threadIdx.x;
 
   const int64_t base = a.seq_start[qi / a.q_per_seq];
@@ -180,18 +232,40 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     const int64_t nblk = (n_vis + 7) / 8;
     const float* bm = a.blockmax + (int64_t)qi * a.nblk_max;
     const int kk = (int)min<int64_t>(a.P, nblk);
-    const bool in_lds = nblk <= kSelLdsKeys;
-    if (in_lds) {
-      for (int64_t i = tid; i < nblk; i += kSelThreads) sh.keys[i] = float_key(bm[i]);
-      __syncthreads();
+    npool = 0;
+    if (kk > 0 && nblk <= kRegKeys) {
+      RegKeys keys;
+      const int64_t i0 = (int64_t)tid * kKPT;
+      if (i0 + kKPT <= nblk && (((uintptr_t)(bm + i0)) & 15) == 0) {
+        const float4* v = reinterpret_cast<const float4*>(bm + i0);
+#pragma unroll
+        for (int j = 0; j < kKPT / 4; ++j) {
+          const float4 f = v[j];
+          keys.k[4 * j] = float_key(f.x); keys.k[4 * j + 1] = float_key(f.y);
+          keys.k[4 * j + 2] = float_key(f.z); keys.k[4 * j + 3] = float_key(f.w);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kKPT; ++j) keys.k[j] = i0 + j < nblk ? float_key(bm[i0 + j]) : 0u;
+      }
+      uint32_t T; int take_eq;
+      radix_threshold(sh, keys, kk, T, take_eq);
+      npool = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) {
+        const int32_t b = (int32_t)(i0 + j);
+        sh.pool[slot] = b;
+        pool_row[slot] = b;
+      });
+    } else if (kk > 0) {
+      const int64_t per = (nblk + kSelThreads - 1) / kSelThreads;
+      GlobalKeys keys{bm, min<int64_t>((int64_t)tid * per, nblk), min<int64_t>((int64_t)tid * per + per, nblk)};
+      uint32_t T; int take_eq;
+      radix_threshold(sh, keys, kk, T, take_eq);
+      npool = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) {
+        const int32_t b = (int32_t)(keys.lo + j);
+        sh.pool[slot] = b;
+        pool_row[slot] = b;
+      });
     }
-    auto bkey = [&](int64_t i) -> uint32_t { return in_lds ? sh.keys[i] : float_key(bm[i]); };
-    uint32_t T = 0; int take_eq = 0;
-    if (kk > 0) radix_threshold(sh, bkey, nblk, kk, T, take_eq);
-    npool = kk > 0 ? compact_selected(sh, bkey, nblk, T, take_eq, [&](int slot, int64_t i) {
-      sh.pool[slot] = (int32_t)i;
-      pool_row[slot] = (int32_t)i;
-    }) : 0;
     for (int i = npool + tid; i < a.P; i += kSelThreads) pool_row[i] = -1;
     if (tid == 0) a.n_pool[qi] = npool;
     __syncthreads();
@@ -202,47 +276,59 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     __syncthreads();
   }
 
-  // ---- pool positions -> top-k (keys for slot j = block pool[j/8], token j%8)
-  const int64_t nslot = (int64_t)npool * 8;
-  const float* sc = REINDEX ? a.scores + (int64_t)qi * a.P * 8 : a.scores + (int64_t)qi * a.max_ctx;
-  int nvalid = 0;
-  for (int64_t j = tid; j < nslot; j += kSelThreads) {
-    const int64_t b = sh.pool[j >> 3];
-    const int64_t t = b * 8 + (j & 7);
-    const bool ok = b >= 0 && t < n_vis;
-    sh.keys[j] = ok ? float_key(REINDEX ? sc[j] : sc[t]) : 0u;
-    nvalid += ok;
+  // ---- pool positions -> top-k. Candidate j (< npool*8) is position
+  // pool[j/8]*8 + j%8; thread t owns candidates 16t .. 16t+15 (two blocks).
+  RegKeys keys;
+  int nvalid_local = 0;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int jb = 2 * tid + half;                     // pool slot
+    const int64_t b = jb < npool ? (int64_t)sh.pool[jb] : -1;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (REINDEX) {
+      if (jb < npool) {
+        const float4* v = reinterpret_cast<const float4*>(a.scores + ((int64_t)qi * a.P + jb) * 8);
+        const float4 f0 = v[0], f1 = v[1];
+        s[0] = f0.x; s[1] = f0.y; s[2] = f0.z; s[3] = f0.w; s[4] = f1.x; s[5] = f1.y; s[6] = f1.z; s[7] = f1.w;
+      }
+    } else if (b >= 0 && b * 8 + 8 <= n_vis && ((a.max_ctx & 3) == 0)) {
+      const float4* v = reinterpret_cast<const float4*>(a.scores + (int64_t)qi * a.max_ctx + b * 8);
+      const float4 f0 = v[0], f1 = v[1];
+      s[0] = f0.x; s[1] = f0.y; s[2] = f0.z; s[3] = f0.w; s[4] = f1.x; s[5] = f1.y; s[6] = f1.z; s[7] = f1.w;
+    } else if (b >= 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] = b * 8 + e < n_vis ? a.scores[(int64_t)qi * a.max_ctx + b * 8 + e] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool ok = b >= 0 && b * 8 + e < n_vis;
+      keys.k[8 * half + e] = ok ? float_key(s[e]) : 0u;
+      nvalid_local += ok;
+    }
   }
-  int d0, d1, d2;
-  block_scan2(sh, nvalid, 0, d0, d1, nvalid, d2);
+  int nvalid;
+  block_exclusive_scan(sh, nvalid_local, nvalid);
   const int kk = min(a.k, nvalid);
-  auto tkey = [&](int64_t j) -> uint32_t { return sh.keys[j]; };
-  uint32_t T = 0; int take_eq = 0;
-  if (kk > 0) radix_threshold(sh, tkey, nslot, kk, T, take_eq);
   int32_t* out = a.idx_out + (int64_t)qi * a.k;
-  const int nsel = kk > 0 ? compact_selected(sh, tkey, nslot, T, take_eq, [&](int slot, int64_t j) {
-    out[slot] = sh.pool[j >> 3] * 8 + (int32_t)(j & 7);
-  }) : 0;
+  int nsel = 0;
+  if (kk > 0) {
+    uint32_t T; int take_eq;
+    radix_threshold(sh, keys, kk, T, take_eq);
+    nsel = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) {
+      const int jb = 2 * tid + (j >> 3);
+      out[slot] = sh.pool[jb] * 8 + (j & 7);
+    });
+  }
   for (int i = nsel + tid; i < a.k; i += kSelThreads) out[i] = -1;
   if (tid == 0) a.n_idx[qi] = nsel;
 }
 
-size_t select_lds_bytes() { return sizeof(SelShared); }
-
 hipError_t launch_select(const SelectArgs& a, int n_q, bool reindex, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
-  const size_t lds = sizeof(SelShared);
-  // More than 64 KB of dynamic LDS must be requested per kernel (once per process).
-  static const hipError_t attr = [&] {
-    hipError_t e1 = hipFuncSetAttribute((const void*)select_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipError_t e2 = hipFuncSetAttribute((const void*)select_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    return e1 != hipSuccess ? e1 : e2;
-  }();
-  if (attr != hipSuccess) return attr;
   if (reindex)
-    select_kernel<true><<<dim3(n_q), dim3(kSelThreads), lds, stream>>>(a);
+    select_kernel<true><<<dim3(n_q), dim3(kSelThreads), 0, stream>>>(a);
   else
-    select_kernel<false><<<dim3(n_q), dim3(kSelThreads), lds, stream>>>(a);
+    select_kernel<false><<<dim3(n_q), dim3(kSelThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
