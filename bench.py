@@ -30,6 +30,13 @@ sys.path.insert(0, ROOT)
 METRIC = "decode queries/s + HBM GB/s (% of peak), Full-layer sparse attn @128K ctx"
 HBM_PEAK_GBPS = 8000.0
 
+# HBM bytes per scan launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes over this
+# command, each scaled by the counter's reading for a plain 1 GiB copy (x1.99994 and
+# x1.0). Valid only for the scan sources they were taken on: a change to any of them
+# turns the figure into null until the counters are taken again.
+SCAN_SOURCES = ("scan.hip", "kernels.h", "common.h")
+SCAN_TRAFFIC = {"sources_sha256_16": "5b972c1feaf98117", "bytes_per_launch": 1093948597}
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -59,9 +66,19 @@ def algorithmic_bytes(cfg):
     return {"scan": scan, "select": select, "attn": attn, "append": append, "layer": layer}
 
 
-def cpu_baseline(cfg, n_sample):
+def scan_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for name in SCAN_SOURCES:
+        with open(os.path.join(ROOT, "sparse_indexer_fp4_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return SCAN_TRAFFIC["bytes_per_launch"] if h.hexdigest()[:16] == SCAN_TRAFFIC["sources_sha256_16"] else None
+
+
+def cpu_baseline(cfg, n_sample, min_seconds=10.0):
     """The oracle, as it stands, on n_sample queries of the same workload:
-    Full-layer indexer + attention per query. Input generation is not timed."""
+    Full-layer indexer + attention per query, passes over the sample repeated until
+    min_seconds of CPU work. Input generation is not timed."""
     import numpy as np
     import torch
     from synth import bf16_to_f64
@@ -85,14 +102,17 @@ def cpu_baseline(cfg, n_sample):
     # timed region only as the oracle's codec input; their generation is timed
     # separately and subtracted.
     t_gen = 0.0
+    done = 0
     t0 = time.perf_counter()
-    for (s, p, krows, q, w, Q, wk, wv) in prepared:
-        pool, idx, _ = indexer.index_full(q, w, krows, p, cfg.P, cfg.k)
-        tg = time.perf_counter()
-        x = bf16_to_f64(wl.kv_rows(cfg, s, torch.from_numpy(idx)))
-        t_gen += time.perf_counter() - tg
-        rows = fp4.dequantize_rows(*fp4.quantize_rows(x))
-        attention.attend(Q, rows, wk, wv, cfg.scale)
+    while done == 0 or time.perf_counter() - t0 - t_gen < min_seconds:
+        for (s, p, krows, q, w, Q, wk, wv) in prepared:
+            pool, idx, _ = indexer.index_full(q, w, krows, p, cfg.P, cfg.k)
+            tg = time.perf_counter()
+            x = bf16_to_f64(wl.kv_rows(cfg, s, torch.from_numpy(idx)))
+            t_gen += time.perf_counter() - tg
+            rows = fp4.dequantize_rows(*fp4.quantize_rows(x))
+            attention.attend(Q, rows, wk, wv, cfg.scale)
+            done += 1
     dt = time.perf_counter() - t0 - t_gen
     threads = torch.get_num_threads()
     try:
@@ -101,9 +121,10 @@ def cpu_baseline(cfg, n_sample):
         threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [threads])
     except Exception:
         pass
-    return {"value": n_sample / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_sample} of the 32 queries of decode128k (Full-layer indexer + attention per query, "
-                      f"float64 numpy; {dt:.1f} s; input generation excluded)"}
+    return {"value": done / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} query evaluations ({done // n_sample} passes over {n_sample} of the 32 queries of "
+                      f"decode128k; Full-layer indexer + attention per query, float64 numpy; {dt:.1f} s; "
+                      f"input generation excluded)"}
 
 
 def main():
@@ -112,6 +133,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-sample", type=int, default=32, help="queries timed on the oracle (0: skip)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes, --steps times (calibrates "
+                         "the HBM byte counters against a kernel of known traffic), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the decode batch shards by query "
@@ -126,8 +150,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    cfg = wl.CONFIGS["decode128k"]
     dev = torch.device("cuda:0")
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {src.numel() * 4} bytes {args.steps} times")
+        return
+    cfg = wl.CONFIGS["decode128k"]
     t0 = time.perf_counter()
     log(f"generating {cfg.name} inputs on the GPU")
     dw = DeviceWorkload(cfg, dev)
@@ -210,7 +242,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "indexer scan (fp4kv_index_scores)",
                      "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": scan_gbps / HBM_PEAK_GBPS, "traffic": None},
+                     "frac": scan_gbps / HBM_PEAK_GBPS, "traffic": scan_traffic()},
         "detail": {"ms_per_launch": per, "algorithmic_bytes": nbytes,
                    "layer_hbm_gbps": layer_gbps, "layer_frac_of_peak": layer_gbps / HBM_PEAK_GBPS},
     }
