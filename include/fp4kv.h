@@ -129,7 +129,8 @@ size_t fp4kv_index_workspace_bytes(int32_t n_q, int64_t max_ctx, int32_t block);
  *   seq_start   (device) int64 [ceil(n_q / q_per_seq)]: first row of each
  *               sequence; query i belongs to sequence i / q_per_seq.
  *   q_pos       (device) int32 [n_q]: position of each query (its causal
- *               limit; decode: context length - 1). Clamped to [0, max_ctx-1];
+ *               limit; decode: context length - 1). Clamped to max_ctx-1; a
+ *               negative position sees no token (empty pool and selection);
  *               rows at or past total_rows are treated as not visible.
  *   H, D        H in {4, 8, 16}; D in {64, 128}.
  *   max_ctx     host bound: every q_pos < max_ctx (sizes the grid).
@@ -228,7 +229,8 @@ size_t fp4kv_attn_workspace_bytes(int32_t n_q, int32_t Hq, int32_t C, int32_t k,
  *   window branch: the last n_w = min(W, p+1) rows of swa_k[b] / swa_v[b]
  *     (row W-1 is position p), softmax -> (o_w, lse_w).
  *   out = (e^lse_s o_s + e^lse_w o_w) / (e^lse_s + e^lse_w); lse = log of the
- *     denominator (natural log). An empty sparse branch contributes nothing.
+ *     denominator (natural log). An empty sparse branch contributes nothing;
+ *     a query with p < 0 has no rows at all and gets out = 0, lse = -inf.
  *
  *   q          (device) bf16 [B, Hq, C]
  *   codes      (device) uint8 [total_rows, C/2]; scales (device) uint8 [total_rows, C/16]

@@ -43,9 +43,15 @@ def merge(o_s, lse_s, o_w, lse_w):
     """Combine two softmax partitions given their outputs and log-sum-exps.
 
     out = (e^{lse_s} o_s + e^{lse_w} o_w) / (e^{lse_s} + e^{lse_w}), evaluated
-    relative to max(lse_s, lse_w). Returns (out [Hq, C], lse [Hq]).
+    relative to max(lse_s, lse_w). Returns (out [Hq, C], lse [Hq]). With both
+    partitions empty the result is out = 0, lse = -inf (the empty sum).
     """
     M = np.maximum(lse_s, lse_w)
+    if np.isneginf(M).any():
+        # no row in either branch (a query that sees no token): output 0, lse -inf
+        if not np.isneginf(M).all():
+            raise ValueError("heads disagree on whether any row is present")
+        return np.zeros_like(o_s), M.copy()
     a = np.exp(lse_s - M)
     b = np.exp(lse_w - M)
     out = (a[:, None] * o_s + b[:, None] * o_w) / (a + b)[:, None]

@@ -80,10 +80,10 @@ __device__ __forceinline__ QueryInfo query_info(const AttnArgs& a, int qi) {
   QueryInfo r;
   r.kv_base = a.seq_start ? a.seq_start[qi] : a.seq_start_scalar;
   int64_t p = a.q_pos ? (int64_t)a.q_pos[qi] : (int64_t)a.pos0 + qi;
-  r.p = p < 0 ? 0 : p;
+  r.p = p;            // negative: the query sees no token
   int ns = a.n_idx[qi];
   r.n_s = ns < 0 ? 0 : (ns > a.k ? a.k : ns);
-  r.n_w = (int)min<int64_t>(a.W, r.p + 1);
+  r.n_w = p < 0 ? 0 : (int)min<int64_t>(a.W, p + 1);
   r.cs = (r.n_s + kChunk - 1) / kChunk;
   r.cw = (r.n_w + kChunk - 1) / kChunk;
   r.win_row0 = (int64_t)qi * a.win_stride + (a.W - r.n_w);

@@ -38,7 +38,8 @@ typedef const __attribute__((address_space(4))) float* const_f32_ptr;
 __device__ __forceinline__ int64_t visible_rows(const ScanArgs& a, int qi, int64_t& base) {
   base = a.seq_start[qi / a.q_per_seq];
   int64_t p = a.q_pos[qi];
-  p = p < 0 ? 0 : (p >= a.max_ctx ? a.max_ctx - 1 : p);
+  if (p < 0) return 0;                                  // sees no token
+  p = p >= a.max_ctx ? a.max_ctx - 1 : p;
   int64_t n = p + 1;
   int64_t avail = a.total_rows - base;
   if (avail < n) n = avail;

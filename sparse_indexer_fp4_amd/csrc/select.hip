@@ -220,8 +220,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 
   const int64_t base = a.seq_start[qi / a.q_per_seq];
   int64_t p = a.q_pos[qi];
-  p = p < 0 ? 0 : (p >= a.max_ctx ? a.max_ctx - 1 : p);
-  int64_t n_vis = p + 1;
+  p = p >= a.max_ctx ? a.max_ctx - 1 : p;
+  int64_t n_vis = p < 0 ? 0 : p + 1;                    // a negative position sees no token
   if (a.total_rows - base < n_vis) n_vis = a.total_rows - base;
   if (n_vis < 0) n_vis = 0;
 

@@ -295,6 +295,21 @@ def check_causal_visibility():
     assert indexer.pool_positions(np.array([10]), 85).tolist() == [80, 81, 82, 83, 84]
 
 
+def check_empty_query():
+    """A query that sees no token (position -1, e.g. an empty context slot):
+    no scores, an empty pool and selection, and attention over no row at all
+    is the empty sum: output 0, log-sum-exp -inf (no NaN)."""
+    rng = np.random.default_rng(19)
+    q = rng.integers(-8, 9, size=(4, 16)).astype(float); w = np.ones(4)
+    k = rng.integers(-8, 9, size=(40, 16)).astype(float)
+    pool, idx, s = indexer.index_full(q, w, k, -1, 4, 6)
+    assert s.shape[0] == 0 and pool.size == 0 and idx.size == 0
+    assert indexer.index_reindex(q, w, lambda pos: k[pos], np.array([0, 1]), -1, 6).size == 0
+    Q = rng.standard_normal((3, 16)); none = np.zeros((0, 16))
+    out, lse = attention.attend(Q, none, none, none, 0.25)
+    assert out.shape == (3, 16) and (out == 0).all() and np.isneginf(lse).all()
+
+
 def check_cover_all():
     """When the pool covers every block and k covers every token, every
     visible position is selected."""

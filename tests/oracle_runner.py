@@ -54,8 +54,17 @@ def attend(cfg, i, layer, idx):
 
 
 def within_tolerance(got, ref):
-    """max |got - ref| <= 2e-4 * max |ref| + 1e-6 over the tensor."""
+    """max |got - ref| <= 2e-4 * max |ref| + 1e-6 over the tensor's finite
+    reference entries; infinite entries (the lse of a query with no row) must
+    match exactly. A NaN anywhere fails."""
     ref = np.asarray(ref, dtype=np.float64)
-    err = np.abs(np.asarray(got, dtype=np.float64) - ref).max()
-    tol = 2e-4 * np.abs(ref).max() + 1e-6
-    return err <= tol, err, tol
+    got = np.asarray(got, dtype=np.float64)
+    inf = np.isinf(ref)
+    if inf.any() and not np.array_equal(got[inf], ref[inf]):
+        return False, float("inf"), 0.0
+    fin = ~inf
+    if not fin.any():
+        return True, 0.0, 0.0
+    err = np.abs(got[fin] - ref[fin]).max()
+    tol = 2e-4 * np.abs(ref[fin]).max() + 1e-6
+    return bool(err <= tol), err, tol

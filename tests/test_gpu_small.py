@@ -152,6 +152,20 @@ def test_index_full_ties(fk, gpu):
     _indexer_case(fk, gpu, [3000, 2999, 16], 4, 64, 32, 64, seed=5, lo=-1, hi=1)
 
 
+def test_index_full_empty_contexts(fk, gpu):
+    """Zero-length contexts inside a ragged batch (query position -1): empty
+    pool and selection, and the neighbours' rows stay invisible to them."""
+    _say("index_full empty contexts")
+    _indexer_case(fk, gpu, [3000, 0, 17, 0, 1], 16, 128, 64, 100, seed=21)
+
+
+def test_index_full_all_equal_scores(fk, gpu):
+    """Every key and query equal: all scores tie, so both levels take the
+    lowest blocks / positions (the radix search ends before its first digit)."""
+    _say("index_full all-equal scores")
+    _indexer_case(fk, gpu, [5000, 9, 130], 8, 64, 16, 40, seed=23, lo=1, hi=1)
+
+
 def test_index_full_prefill_positions(fk, gpu):
     """One sequence, many queries at consecutive positions (causal)."""
     _say("index_full prefill-style positions")
@@ -228,6 +242,7 @@ def _attn_case(fk, gpu, lengths, n_idx, Hq, k, W, seed):
     ([5000, 300, 70, 1], [512, 300, 17, 1], 64, 512, 128),   # ragged counts, short windows
     ([2000] * 6, [0, 1, 31, 32, 33, 500], 32, 512, 128),      # empty sparse branch, chunk edges
     ([100000, 3000], [512, 512], 64, 512, 100),        # window not a multiple of 32
+    ([2000, 0, 40], [100, 0, 40], 64, 512, 128),       # a query with no row at all: out 0, lse -inf
 ])
 def test_attention_matches_oracle(fk, gpu, lengths, n_idx, Hq, k, W):
     _say(f"attention lengths={lengths} n_idx={n_idx} Hq={Hq}")
