@@ -1,6 +1,7 @@
 // C ABI of libfp4kv: argument checks, workspace sizing, grid sizing from host
 // scalars, and kernel launches on the caller's stream. The declarations and
 // their contracts are in include/fp4kv.h.
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -115,6 +116,9 @@ static fp4kv_status launch_scores(const void* idx_q, const float* w, const void*
   sa.scores = scores;
   sa.blockmax = blockmax;
   sa.nblk_max = nblk_of(max_ctx, block);
+  // Many queries per sequence share every key: the scan is a dense product on the matrix cores.
+  if (fp4kv::scan_mfma_supported(H, D, q_per_seq) && max_ctx <= INT32_MAX)
+    return hip_status(fp4kv::launch_scan_mfma(sa, H, D, n_q, s), "index scan (matrix cores)");
   return hip_status(fp4kv::launch_scan(sa, H, D, n_q, max_ctx, false, s), "index scan");
 }
 

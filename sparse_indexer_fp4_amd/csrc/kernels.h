@@ -26,6 +26,17 @@ struct ScanArgs {
   int32_t steps;             // 64-token steps per workgroup
 };
 
+// Launch geometry of the matrix-core scan (host-computed).
+struct MfmaScanGrid {
+  int32_t qblocks_per_seq;   // 32-query blocks per sequence
+  int32_t n_qblocks;         // over all sequences
+  int32_t n_ranges;          // token ranges
+  int64_t range_tokens;      // tokens per range, a multiple of 64
+  int32_t per_xcd;           // work items per XCD
+  int32_t H;                 // indexer heads (<= 16; missing heads are zero)
+  int32_t n_q;
+};
+
 struct SelectArgs {
   const int64_t* seq_start;
   const int32_t* q_pos;
@@ -73,6 +84,9 @@ hipError_t launch_quantize_append(const void* src, int64_t n_rows, int32_t C, co
 bool scan_supported(int H, int D);
 // slots: max_ctx for a Full scan, P*8 for a Reindex scan.
 hipError_t launch_scan(ScanArgs a, int H, int D, int n_q, int64_t slots, bool reindex, hipStream_t stream);
+// Matrix-core Full scan for sequences with many queries (q_per_seq >= 16).
+bool scan_mfma_supported(int H, int D, int q_per_seq);
+hipError_t launch_scan_mfma(ScanArgs a, int H, int D, int n_q, hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, int n_q, bool reindex, hipStream_t stream);
 size_t attn_workspace_bytes(int nq, int Hq, int k, int W);
 hipError_t launch_attn(AttnArgs a, void* ws, hipStream_t stream);

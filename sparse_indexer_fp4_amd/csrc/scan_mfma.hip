@@ -1,0 +1,253 @@
+// Indexer scan for many queries of one sequence (a prefill chunk) on the
+// matrix cores: the same token score s_t = sum_h w_h * max(0, q_h . k_t) and
+// 8-token block maximum as the decode scan.
+// [G] hierarchical sparse indexer paragraph; [T] "Mechanism 4: the hierarchical
+// sparse indexer"; [N] "CSA2: Sharing Main KV, Indexer K, and Top-K Indices
+// Across Layers" (the Full layer scores every visible context token).
+//
+// Queries of one sequence share every key, so q_h . k_t for 16 heads x 16
+// tokens is one v_mfma_f32_16x16x32_bf16 tile per 32 channels: rows = heads
+// (the query fragment, resident in VGPRs), columns = tokens (the key fragment,
+// read from LDS). A lane of the result holds 4 heads of one token; ReLU and the
+// head weights are applied there. The four 16-lane groups' partial sums of two
+// queries x two 16-token tiles are then reduce-scattered with
+// v_permlane32_swap and v_permlane16_swap so that lane l ends with the full
+// score of query l/32 at token l%32 of the 32-token half-tile.
+//
+// Workgroup = 32 queries of one sequence x one range of tokens: 8 compute waves
+// (4 queries each) and one copy wave. The copy wave streams 64-token key tiles
+// HBM -> LDS with global_load_lds into a 3-deep ring, XOR-swizzled so that the
+// compute waves' 16-byte fragment reads are free of bank conflicts. It is the
+// only wave that loads, so its vmcnt waits count its tile loads alone (the
+// compute waves' score stores never hold them up). One barrier per tile:
+// before it the copy wave has waited for the next tile and the compute waves
+// have finished the current one; the tile after next is then loaded into the
+// slot the finished tile leaves free.
+//
+// Work items (query block, token range) are laid out so that the workgroups
+// an XCD runs together share one token range, which then streams through that
+// XCD's L2 once.
+//
+// Integer-valued bf16 inputs make every product and partial sum exact in fp32
+// while below 2^24, so the scores equal the decode scan's bit for bit.
+#include "kernels.h"
+
+namespace fp4kv {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kMQ = 32;                       // queries per workgroup
+constexpr int kMWaves = 8;                    // compute waves, 4 queries each
+constexpr int kMThreads = (kMWaves + 1) * 64; // + the copy wave
+constexpr int kMTile = 64;                    // tokens per LDS tile
+constexpr int kMRing = 3;                     // tiles in the ring
+
+__device__ __forceinline__ int64_t mq_visible(const ScanArgs& a, int q, int64_t base) {
+  int64_t p = a.q_pos[q];
+  if (p < 0) return 0;                        // sees no token
+  p = p >= a.max_ctx ? a.max_ctx - 1 : p;
+  int64_t n = p + 1;
+  const int64_t avail = a.total_rows - base;
+  if (avail < n) n = avail;
+  return n < 0 ? 0 : n;
+}
+
+// max(x, 0) for the finite values here, as one v_med3 (no NaN quieting step).
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f); }
+
+// Maximum over each aligned group of 8 lanes, left in every lane of the group
+// (DPP: swap neighbours, swap pairs, then mirror the halves of each 8 lanes).
+__device__ __forceinline__ float max8(float v) {
+  int x = __float_as_int(v);
+  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false)), 3.402823466e38f));
+  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false)), 3.402823466e38f));
+  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false)), 3.402823466e38f));
+  return __int_as_float(x);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D>
+__global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a, MfmaScanGrid g) {
+  constexpr int NCH = D / 8;                  // 16-byte chunks per key row
+  constexpr int KS = D / 32;                  // 32-channel MFMA k-steps
+  constexpr int NL = kMTile * NCH / 64;       // copy instructions per tile
+  __shared__ __attribute__((aligned(16))) uint4 ring[kMRing][kMTile * NCH];
+  __shared__ int32_t nvis[kMQ];
+
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int wi = (blockIdx.x % 8) * g.per_xcd + blockIdx.x / 8;
+  const int r = wi / g.n_qblocks, qb = wi % g.n_qblocks;
+  if (r >= g.n_ranges) return;                // padding item (uniform)
+  const int s = qb / g.qblocks_per_seq;
+  const int q0 = s * a.q_per_seq + (qb % g.qblocks_per_seq) * kMQ;
+  const int q1 = min(min(q0 + kMQ, (s + 1) * a.q_per_seq), g.n_q);
+  const int64_t base = a.seq_start[s];
+
+  if (threadIdx.x < kMQ) {
+    const int q = q0 + threadIdx.x;
+    nvis[threadIdx.x] = q < q1 ? (int32_t)mq_visible(a, q, base) : 0;
+  }
+  __syncthreads();
+  int32_t maxv = 0;
+#pragma unroll
+  for (int i = 0; i < kMQ; ++i) maxv = max(maxv, nvis[i]);
+  const int64_t r0 = (int64_t)r * g.range_tokens;
+  const int64_t r1 = min(r0 + g.range_tokens, (int64_t)maxv);
+  if (r0 >= r1) return;                       // nothing visible in this range (uniform)
+  const int nsteps = (int)((r1 - r0 + kMTile - 1) / kMTile);
+
+  if (wave == kMWaves) {
+    // ---------------- copy wave
+    const char* kseq = reinterpret_cast<const char*>(a.idx_k + base * D);
+    const int64_t last = maxv - 1;            // rows past every query's visibility are never read back
+    auto issue = [&](int st) {
+      const int64_t t0 = r0 + (int64_t)st * kMTile;
+      uint4* dst = ring[st % kMRing];
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int slot = i * 64 + lane, tok = slot / NCH, c = (slot % NCH) ^ (tok % NCH);
+        int64_t t = t0 + tok;
+        t = t > last ? last : t;
+        __builtin_amdgcn_global_load_lds((const void*)(kseq + t * (D * 2) + c * 16),
+                                         (__attribute__((address_space(3))) void*)&dst[i * 64], 16, 0, 0);
+      }
+    };
+    issue(0);
+    if (nsteps > 1) { issue(1); wait_vm<NL>(); } else { wait_vm<0>(); }
+    tile_barrier();
+    for (int st = 0; st < nsteps; ++st) {
+      if (st + 2 < nsteps) { issue(st + 2); wait_vm<NL>(); } else { wait_vm<0>(); }
+      tile_barrier();
+    }
+    return;
+  }
+
+  // ---------------- compute waves: queries q0 + 4*wave + j, j = 0..3
+  const int g4 = lane / 16, col = lane % 16;
+  uint4 qa[4][KS];                            // A operand: Q[q][head col][32ks + 8g4 .. +7]
+  float wv[4][4];                             // w[q][4g4 + i]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = q0 + 4 * wave + j;
+    const bool valid = q < q1;
+    const uint4* qp = reinterpret_cast<const uint4*>(a.idx_q + ((int64_t)(valid ? q : q0) * g.H + (col < g.H ? col : 0)) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 v = qp[4 * ks + g4];
+      qa[j][ks] = (valid && col < g.H) ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g4 + i;
+      wv[j][i] = (valid && h < g.H) ? a.w[(int64_t)q * g.H + h] : 0.0f;
+    }
+  }
+  // visible-token limits of the queries whose scores this lane will hold (query 2jp + lane/32)
+  const int32_t lim[2] = {nvis[4 * wave + (lane >> 5)], nvis[4 * wave + 2 + (lane >> 5)]};
+  tile_barrier();
+
+  for (int st = 0; st < nsteps; ++st) {
+    const uint4* tile = ring[st % kMRing];
+    const int64_t t0 = r0 + (int64_t)st * kMTile;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint4 bf[2][KS];                        // B operand: K[token col of tile tt][32ks + 8g4 .. +7]
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int tok = 32 * half + 16 * tt + col;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bf[tt][ks] = tile[tok * NCH + ((4 * ks + g4) ^ (tok % NCH))];
+      }
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) {
+        v4f acc[2][2];                        // [query of the pair][16-token tile]
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) acc[qq][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+              acc[qq][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, qa[2 * jp + qq][ks]),
+                                                                    __builtin_bit_cast(v8bf, bf[tt][ks]),
+                                                                    acc[qq][tt], 0, 0, 0);
+        // lane: heads 4g4..4g4+3 of token col; weighted ReLU sum over them
+        float p[2][2];
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            float v = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v = fmaf(wv[2 * jp + qq][i], relu(acc[qq][tt][i]), v);
+            p[qq][tt] = v;
+          }
+        // lanes 0-31 <- query A, lanes 32-63 <- query B (head groups g, g+2 summed)
+        const auto xa = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0][0]), __float_as_uint(p[1][0]), false, false);
+        const auto xb = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0][1]), __float_as_uint(p[1][1]), false, false);
+        const float sa = __uint_as_float(xa[0]) + __uint_as_float(xa[1]);
+        const float sb = __uint_as_float(xb[0]) + __uint_as_float(xb[1]);
+        // rows of 16 lanes: (A, tile 0), (A, tile 1), (B, tile 0), (B, tile 1); all four head groups summed
+        const auto yy = __builtin_amdgcn_permlane16_swap(__float_as_uint(sa), __float_as_uint(sb), false, false);
+        const float y = __uint_as_float(yy[0]) + __uint_as_float(yy[1]);
+
+        const int64_t t = t0 + 32 * half + (lane & 31);
+        const bool vis = t < lim[jp];
+        const int64_t q = q0 + 4 * wave + 2 * jp + (lane >> 5);
+        if (vis) a.scores[q * a.max_ctx + t] = y;
+        const float bm = max8(vis ? y : -3.402823466e38f);
+        if ((lane & 7) == 0 && vis) a.blockmax[q * a.nblk_max + (t >> 3)] = bm;
+      }
+    }
+    tile_barrier();
+  }
+}
+
+bool scan_mfma_supported(int H, int D, int q_per_seq) {
+  return q_per_seq >= 16 && H <= 16 && (D == 64 || D == 128);
+}
+
+hipError_t launch_scan_mfma(ScanArgs a, int H, int D, int n_q, hipStream_t stream) {
+  if (n_q == 0 || a.max_ctx == 0) return hipSuccess;
+  MfmaScanGrid g{};
+  g.H = H;
+  g.n_q = n_q;
+  const int n_seq = (n_q + a.q_per_seq - 1) / a.q_per_seq;
+  g.qblocks_per_seq = (a.q_per_seq + kMQ - 1) / kMQ;
+  g.n_qblocks = n_seq * g.qblocks_per_seq;
+  // About 8,192 tokens per range; shorter ranges when there are few query
+  // blocks, so that the launch still spans the chip several times.
+  int64_t n_ranges = (a.max_ctx + 4095) / 8192;
+  const int64_t want = (1024 + g.n_qblocks - 1) / g.n_qblocks;
+  if (n_ranges < want) n_ranges = want;
+  const int64_t max_ranges = (a.max_ctx + 511) / 512;
+  if (n_ranges > max_ranges) n_ranges = max_ranges;
+  if (n_ranges < 1) n_ranges = 1;
+  const int64_t per = (a.max_ctx + n_ranges - 1) / n_ranges;
+  g.range_tokens = (per + kMTile - 1) / kMTile * kMTile;
+  g.n_ranges = (int32_t)((a.max_ctx + g.range_tokens - 1) / g.range_tokens);
+  const int64_t items = (int64_t)g.n_ranges * g.n_qblocks;
+  g.per_xcd = (int32_t)((items + 7) / 8);
+  const dim3 grid((uint32_t)(8 * (int64_t)g.per_xcd));
+  if (D == 128)
+    scan_mfma_kernel<128><<<grid, dim3(kMThreads), 0, stream>>>(a, g);
+  else if (D == 64)
+    scan_mfma_kernel<64><<<grid, dim3(kMThreads), 0, stream>>>(a, g);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace fp4kv

@@ -173,6 +173,45 @@ def test_index_full_prefill_positions(fk, gpu):
     _indexer_case(fk, gpu, [L], 16, 128, 16, 40, seed=9, q_per_seq=37, positions=list(range(L - 37, L)))
 
 
+@pytest.mark.parametrize("H,D", [(16, 128), (4, 64), (8, 128)])
+def test_index_full_many_queries_per_sequence(fk, gpu, H, D):
+    """Sequences with >= 16 queries each take the matrix-core scan: ragged
+    lengths, a 32-query block cut short by the sequence, positions anywhere in
+    the sequence (and -1)."""
+    _say(f"index_full many queries per sequence H={H} D={D}")
+    lengths, q_per_seq = [2500, 9000, 40], 48
+    rng = np.random.default_rng(H * 100 + D)
+    positions = []
+    for L in lengths:
+        positions += rng.integers(-1, L, size=q_per_seq).tolist()
+    _indexer_case(fk, gpu, lengths, H, D, 64, 100, seed=31 + H, q_per_seq=q_per_seq, positions=positions)
+
+
+@pytest.mark.parametrize("H,D", [(16, 128), (4, 64)])
+def test_scores_matrix_core_scan_equals_decode_scan(fk, gpu, H, D):
+    """Every token score and block maximum of the matrix-core scan (many queries
+    per sequence) equals the per-query scan's bit for bit; unwritten entries stay
+    untouched in both."""
+    _say(f"scores: matrix-core scan vs per-query scan H={H} D={D}")
+    L, T = 20000, 100
+    kk = int_tensor_bf16(41, "k", 0, (L, D), -8, 8).to(gpu)
+    q = int_tensor_bf16(41, "q", 0, (T, H, D), -8, 8).to(gpu)
+    w = torch.randint(1, 9, (T, H), generator=torch.Generator().manual_seed(41)).to(torch.float32).to(gpu)
+    pos = torch.from_numpy(np.random.default_rng(41).integers(-1, L, size=T).astype(np.int32)).to(gpu)
+    max_ctx = L
+    nblk = (max_ctx + 7) // 8
+    outs = []
+    for q_per_seq, starts in ((T, torch.zeros(1, dtype=torch.int64)), (1, torch.zeros(T, dtype=torch.int64))):
+        sc = torch.full((T, max_ctx), float("nan"), device=gpu)
+        bm = torch.full((T, nblk), float("nan"), device=gpu)
+        fk.fp4kv_index_scores(q, w, kk, starts.to(gpu), pos, q_per_seq, max_ctx, scores=sc, blockmax=bm)
+        outs.append((sc.view(torch.int32).cpu(), bm.view(torch.int32).cpu()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    written = ~torch.isnan(outs[0][0].view(torch.float32))
+    assert int(written.sum()) == int((pos.cpu().clamp(min=-1) + 1).sum())
+
+
 def test_index_reindex_matches_oracle(fk, gpu):
     _say("index_reindex")
     lengths = [9000, 33, 5000]
