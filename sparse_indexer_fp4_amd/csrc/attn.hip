@@ -32,13 +32,9 @@
 
 namespace fp4kv {
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
 constexpr int kAttnC = 512;       // channels (the kernels are written for 512)
 constexpr int kChunk = 32;        // rows per chunk
 constexpr int kItems = kChunk / 2 * (kAttnC / 16);  // (row pair, 16-channel group) items = 512
-
 
 struct AttnShared {
   uint4 kbuf[kChunk * kAttnC / 8];       // row-major bf16, 16-byte units swizzled: 32 KB

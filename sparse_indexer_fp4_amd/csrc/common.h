@@ -7,6 +7,13 @@ namespace fp4kv {
 
 constexpr int kWave = 64;
 
+// Operand and result types of v_mfma_f32_16x16x32_bf16.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// max(x, 0) for finite x as one v_med3 (fmaxf would add a NaN-quieting step).
+__device__ __forceinline__ float relu_f(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f); }
+
 // bfloat16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }

@@ -34,9 +34,6 @@
 
 namespace fp4kv {
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
 constexpr int kMQ = 32;                       // queries per workgroup
 constexpr int kMWaves = 8;                    // compute waves, 4 queries each
 constexpr int kMThreads = (kMWaves + 1) * 64; // + the copy wave
@@ -52,9 +49,6 @@ __device__ __forceinline__ int64_t mq_visible(const ScanArgs& a, int q, int64_t 
   if (avail < n) n = avail;
   return n < 0 ? 0 : n;
 }
-
-// max(x, 0) for the finite values here, as one v_med3 (no NaN quieting step).
-__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f); }
 
 // Maximum over each aligned group of 8 lanes, left in every lane of the group
 // (DPP: swap neighbours, swap pairs, then mirror the halves of each 8 lanes).
@@ -191,7 +185,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a, MfmaSc
           for (int tt = 0; tt < 2; ++tt) {
             float v = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v = fmaf(wv[2 * jp + qq][i], relu(acc[qq][tt][i]), v);
+            for (int i = 0; i < 4; ++i) v = fmaf(wv[2 * jp + qq][i], relu_f(acc[qq][tt][i]), v);
             p[qq][tt] = v;
           }
         // lanes 0-31 <- query A, lanes 32-63 <- query B (head groups g, g+2 summed)
