@@ -15,15 +15,20 @@
 //
 // The sparse rows and the window rows form one softmax over their union; by
 // the log-sum-exp identity this equals merging the two branch softmaxes by
-// their log-sum-exps.
+// their log-sum-exps. The running maximum is only moved (and O, l rescaled)
+// when a chunk's maximum exceeds it by more than 2^8; otherwise P is formed
+// against the old maximum (values up to 2^8, still exact after the hi/lo
+// split), so the 128 accumulators per lane are normally touched by MFMA only.
 //
 // Workgroup = (query, split); one wave per group of 16 heads. A split takes
-// every n_split-th 32-row chunk. Each chunk is dequantised once into LDS, in a
-// row-major copy (the K operand of S^T = K Q^T) and a channel-major copy (the
-// V^T operand of O^T = V^T P^T), both XOR-swizzled against bank conflicts;
-// the raw bytes of the next chunk are loaded into registers while the current
-// one is computed (window chunks, bf16 and four times larger, are read
-// when committed). Chunk rows 2j and 2j+1 are the j-th rows of the two
+// every n_split-th 32-row chunk. Each chunk is dequantised once into LDS by
+// the whole workgroup, one (8 rows x 8 channels) item per thread: the codes of
+// a row are read as one coalesced 256-byte line per wave, E2M1 magnitudes come
+// from a byte table (v_perm), and the item is written as a row-major copy (the
+// K operand of S^T = K Q^T) and a channel-major copy (the V^T operand of
+// O^T = V^T P^T), both in 16-byte units placed to avoid bank conflicts. The
+// raw bytes of the next sparse chunk are loaded into registers while the
+// current one is computed. Chunk rows 2j and 2j+1 are the j-th rows of the two
 // 16-row MFMA tiles, so each lane's eight P values are exactly the eight rows
 // its P^T operand needs. With one split the result is written directly;
 // otherwise (m, l, O) partials go to the workspace and a combine kernel merges
@@ -34,34 +39,43 @@ namespace fp4kv {
 
 constexpr int kAttnC = 512;       // channels (the kernels are written for 512)
 constexpr int kChunk = 32;        // rows per chunk
-constexpr int kItems = kChunk / 2 * (kAttnC / 16);  // (row pair, 16-channel group) items = 512
+constexpr int kItems = (kChunk / 8) * (kAttnC / 8);   // (8-row, 8-channel) items = 256
 
 struct AttnShared {
-  uint4 kbuf[kChunk * kAttnC / 8];       // row-major bf16, 16-byte units swizzled: 32 KB
-  uint4 vt[kAttnC * kChunk / 8];         // channel-major bf16 [ch][32 slots]: 32 KB
+  uint4 kbuf[kChunk * kAttnC / 8];       // row-major bf16 in 16-byte units: 32 KB
+  uint4 vt[kAttnC * kChunk / 8];         // channel-major bf16, 8 rows per unit: 32 KB
   uint32_t valid;                        // bit r: chunk row r is a real row
 };
 
-// 16-byte unit of (row, unit) in kbuf, and of (ch, slot group) in vt.
+// 16-byte unit holding channels 8u..8u+7 of chunk row `row`. Rows of equal
+// parity (one MFMA tile) spread over all 16 bank groups.
 __device__ __forceinline__ int kbuf_unit(int row, int u) { return row * 64 + (u ^ ((row >> 1) & 15)); }
-__device__ __forceinline__ int vt_unit(int ch, int g) { return ch * 4 + (g ^ (((ch >> 5) ^ (ch >> 2)) & 3)); }
-
-// E2M1 magnitude code (3 bits) -> fp32 value.
-__device__ __forceinline__ float e2m1_mag(uint32_t m) {
-  // 0, 0.5, 1, 1.5, 2, 3, 4, 6
-  float f = __uint_as_float((((m >> 1) + 126u) << 23) | ((m & 1u) << 22));
-  return m >= 2u ? f : 0.5f * (float)m;
+// 16-byte unit holding rows 8q..8q+7 of channel ch. Channels are permuted within
+// aligned groups of 4 and the row quarter is flipped, so that both the 8 channels
+// 8c+e (c = 0..7) written together and the 8 consecutive channels read together
+// land in distinct bank groups.
+__device__ __forceinline__ int vt_unit(int ch, int q) {
+  const int pc = ch ^ ((ch >> 3) & 3);
+  const int f = ((ch >> 2) ^ (ch >> 5)) & 1;
+  return pc * 4 + (q ^ f);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+// Half the value of an E4M3 scale code (sign bit never set): exact in fp32.
+__device__ __forceinline__ float e4m3_half(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e ? __uint_as_float(((e + 119u) << 23) | (m << 20)) : (float)m * 0x1p-10f;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   // exact here: dequantised values fit in bf16
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Raw FP4 bytes of one item (two rows x 16 channels), prefetched into registers.
+// Raw FP4 bytes of one item: channels 8c..8c+7 of 8 consecutive rows.
 struct RawItem {
-  uint2 code[2];      // 8 code bytes per row
-  uint32_t scale[2];  // scale byte per row
+  uint32_t code[8];   // 8 nibbles per row
+  uint32_t scale[8];  // the row's scale byte for these channels
 };
 
 struct QueryInfo {
@@ -95,22 +109,43 @@ __device__ __forceinline__ int64_t sparse_row(const AttnArgs& a, const QueryInfo
   return row < a.total_rows ? row : -1;
 }
 
+// Item `item` of a chunk: row group (8 rows) and channel group (8 channels).
+// Row groups are wave-uniform: a wave covers whole rows.
+__device__ __forceinline__ int item_rows(int item) { return __builtin_amdgcn_readfirstlane(item >> 6); }
+
 // Prefetch the raw bytes of sparse chunk c (window chunks are read at commit time).
 template <int NW>
-__device__ __forceinline__ void load_chunk(const AttnArgs& a, const QueryInfo& Q, int qi, int c, RawItem (&raw)[kItems / (64 * NW)]) {
+__device__ __forceinline__ void load_chunk(const AttnArgs& a, const QueryInfo& Q, int qi, int c,
+                                           RawItem (&raw)[kItems / (64 * NW)]) {
   constexpr int PER = kItems / (64 * NW);
   if (c >= Q.cs) return;
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
     const int item = threadIdx.x + it * 64 * NW;
-    const int rp = item % 16, g = item / 16;          // row pair, 16-channel group
+    const int rg = item_rows(item), cg = item & 63;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t row = sparse_row(a, Q, qi, c * kChunk + 2 * rp + h);
+    for (int r = 0; r < 8; ++r) {
+      const int64_t row = sparse_row(a, Q, qi, c * kChunk + 8 * rg + r);
       const int64_t rr = row < 0 ? 0 : row;
-      raw[it].code[h] = *reinterpret_cast<const uint2*>(a.codes + rr * (kAttnC / 2) + g * 8);
-      raw[it].scale[h] = row < 0 ? 0u : (uint32_t)a.scales[rr * (kAttnC / 16) + g];
+      const uint32_t code = *reinterpret_cast<const uint32_t*>(a.codes + rr * (kAttnC / 2) + 4 * cg);
+      const uint32_t sc = a.scales[rr * (kAttnC / 16) + (cg >> 1)];
+      raw[it].code[r] = row < 0 ? 0u : code;
+      raw[it].scale[r] = row < 0 ? 0u : sc;
     }
+  }
+}
+
+// Write one item (8 rows x 8 channels as bf16 pairs d[row][pair]) into both copies.
+__device__ __forceinline__ void store_item(AttnShared& sh, int rg, int cg, const uint32_t (&d)[8][4]) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) sh.kbuf[kbuf_unit(8 * rg + r, cg)] = make_uint4(d[r][0], d[r][1], d[r][2], d[r][3]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high / low bf16 of each pair
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_perm(d[2 * i + 1][e >> 1], d[2 * i][e >> 1], sel);
+    sh.vt[vt_unit(8 * cg + e, rg)] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -122,55 +157,59 @@ __device__ __forceinline__ void commit_chunk(AttnShared& sh, const QueryInfo& Q,
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
     const int item = threadIdx.x + it * 64 * NW;
-    const int rp = item % 16, g = item / 16;
-    uint32_t kv[2][8];   // [row][channel pair] bf16 pairs for channels 16g .. 16g+15
-    uint32_t vv[2][8];
+    const int rg = item_rows(item), cg = item & 63;
+    uint32_t d[8][4];
+    if (sparse) {
+      // twice the E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 as bytes
+      constexpr uint32_t lut_lo = 0x03020100u, lut_hi = 0x0C080604u;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (sparse) {
-        const float s = e4m3_value(raw[it].scale[h]);
-        const uint32_t w0 = raw[it].code[h].x, w1 = raw[it].code[h].y;
+      for (int r = 0; r < 8; ++r) {
+        const uint32_t code = raw[it].code[r];
+        const float sh2 = e4m3_half(raw[it].scale[r]);
+        const uint32_t me = __builtin_amdgcn_perm(lut_hi, lut_lo, code & 0x07070707u);         // even channels
+        const uint32_t mo = __builtin_amdgcn_perm(lut_hi, lut_lo, (code >> 4) & 0x07070707u);  // odd channels
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t byte = ((e < 4 ? w0 : w1) >> (8 * (e & 3))) & 0xFFu;
-          const uint32_t n0 = byte & 15u, n1 = byte >> 4;
-          float f0 = e2m1_mag(n0 & 7u) * s, f1 = e2m1_mag(n1 & 7u) * s;
-          f0 = (n0 & 8u) ? -f0 : f0;
-          f1 = (n1 & 8u) ? -f1 : f1;
-          kv[h][e] = pack_bf16(f0, f1);
-          vv[h][e] = kv[h][e];
+        for (int j = 0; j < 4; ++j) {
+          float f0 = (float)((me >> (8 * j)) & 0xFFu) * sh2;
+          float f1 = (float)((mo >> (8 * j)) & 0xFFu) * sh2;
+          // sign bits of nibbles 2j (bit 8j+3) and 2j+1 (bit 8j+7)
+          f0 = __uint_as_float(__float_as_uint(f0) | ((code << (28 - 8 * j)) & 0x80000000u));
+          f1 = __uint_as_float(__float_as_uint(f1) | ((code << (24 - 8 * j)) & 0x80000000u));
+          d[r][j] = pack_bf16x2(f0, f1);
         }
-      } else {
-        const int wr = (c - Q.cs) * kChunk + 2 * rp + h;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int wr = (c - Q.cs) * kChunk + 8 * rg + r;
         const bool ok = wr < Q.n_w;
         const int64_t row = Q.win_row0 + (ok ? wr : 0);
-        const uint4* kp = reinterpret_cast<const uint4*>(a.swa_k + row * kAttnC + g * 16);
-        const uint4* vp = reinterpret_cast<const uint4*>(a.swa_v + row * kAttnC + g * 16);
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        const uint4 k0 = ok ? kp[0] : z, k1 = ok ? kp[1] : z;
-        const uint4 v0 = ok ? vp[0] : z, v1 = ok ? vp[1] : z;
-        kv[h][0] = k0.x; kv[h][1] = k0.y; kv[h][2] = k0.z; kv[h][3] = k0.w;
-        kv[h][4] = k1.x; kv[h][5] = k1.y; kv[h][6] = k1.z; kv[h][7] = k1.w;
-        vv[h][0] = v0.x; vv[h][1] = v0.y; vv[h][2] = v0.z; vv[h][3] = v0.w;
-        vv[h][4] = v1.x; vv[h][5] = v1.y; vv[h][6] = v1.z; vv[h][7] = v1.w;
+        const uint4 kv = ok ? *reinterpret_cast<const uint4*>(a.swa_k + row * kAttnC + 8 * cg) : make_uint4(0, 0, 0, 0);
+        d[r][0] = kv.x; d[r][1] = kv.y; d[r][2] = kv.z; d[r][3] = kv.w;
       }
-    }
-    // row-major copy: rows 2rp, 2rp+1; 16-byte units 2g, 2g+1
+      // keys: row-major copy only
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = 2 * rp + h;
-      sh.kbuf[kbuf_unit(r, 2 * g)] = make_uint4(kv[h][0], kv[h][1], kv[h][2], kv[h][3]);
-      sh.kbuf[kbuf_unit(r, 2 * g + 1)] = make_uint4(kv[h][4], kv[h][5], kv[h][6], kv[h][7]);
-    }
-    // channel-major copy: for channel ch, slots 2rp and 2rp+1 (one 32-bit word)
+      for (int r = 0; r < 8; ++r) sh.kbuf[kbuf_unit(8 * rg + r, cg)] = make_uint4(d[r][0], d[r][1], d[r][2], d[r][3]);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int ch = 16 * g + e;
-      const uint32_t lo = (e & 1) ? (vv[0][e >> 1] >> 16) : (vv[0][e >> 1] & 0xFFFFu);
-      const uint32_t hi = (e & 1) ? (vv[1][e >> 1] & 0xFFFF0000u) : (vv[1][e >> 1] << 16);
-      uint32_t* unit = reinterpret_cast<uint32_t*>(&sh.vt[vt_unit(ch, (2 * rp) >> 3)]);
-      unit[((2 * rp) & 7) >> 1] = lo | hi;
+      for (int r = 0; r < 8; ++r) {
+        const int wr = (c - Q.cs) * kChunk + 8 * rg + r;
+        const bool ok = wr < Q.n_w;
+        const int64_t row = Q.win_row0 + (ok ? wr : 0);
+        const uint4 vv = ok ? *reinterpret_cast<const uint4*>(a.swa_v + row * kAttnC + 8 * cg) : make_uint4(0, 0, 0, 0);
+        d[r][0] = vv.x; d[r][1] = vv.y; d[r][2] = vv.z; d[r][3] = vv.w;
+      }
+      // values: channel-major copy only
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_perm(d[2 * i + 1][e >> 1], d[2 * i][e >> 1], sel);
+        sh.vt[vt_unit(8 * cg + e, rg)] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      continue;
     }
+    store_item(sh, rg, cg, d);
   }
   if (threadIdx.x < 64) {
     const int r = threadIdx.x;
@@ -204,7 +243,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
   v4f o[32];
 #pragma unroll
   for (int t = 0; t < 32; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff(), l_run = 0.0f;
+  float m_use = -__builtin_inff(), l_run = 0.0f;   // P is formed as exp2(x - m_use)
 
   RawItem raw[PER];
   int c = split;
@@ -238,14 +277,20 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     for (int i = 1; i < 8; ++i) cm = fmaxf(cm, x[i]);
     cm = fmaxf(cm, __shfl_xor(cm, 16));
     cm = fmaxf(cm, __shfl_xor(cm, 32));
-    const float m_new = fmaxf(m_run, cm);
-    if (m_new == -__builtin_inff()) continue;        // no usable row yet (uniform per head)
-    const float corr = exp2f(m_run - m_new);
+    if (cm == -__builtin_inff() && m_use == -__builtin_inff()) continue;   // nothing usable yet (per head)
+    // move the reference maximum only when this chunk exceeds it by more than 2^8
+    const bool move = cm > m_use + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      const float corr = move ? exp2f(m_use - cm) : 1.0f;
+      if (move) m_use = cm;
+      l_run *= corr;
+#pragma unroll
+      for (int t = 0; t < 32; ++t) o[t] *= corr;
+    }
     float p[8], psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { p[i] = exp2f(x[i] - m_new); psum += p[i]; }
-    l_run = l_run * corr + psum;
-    m_run = m_new;
+    for (int i = 0; i < 8; ++i) { p[i] = exp2f(x[i] - m_use); psum += p[i]; }
+    l_run += psum;
     v8bf phi, plo;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -255,7 +300,6 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < 32; ++t) {
-      o[t] *= corr;
       const uint4 vtile = sh.vt[vt_unit(16 * t + hcol, g)];
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, vtile), phi, o[t], 0, 0, 0);
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, vtile), plo, o[t], 0, 0, 0);
@@ -272,14 +316,14 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     for (int t = 0; t < 32; ++t)
       *reinterpret_cast<float4*>(op + 16 * t + 4 * g) = make_float4(o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv);
     if (a.lse && g == 0)
-      a.lse[(int64_t)qi * a.Hq + head] = l_all > 0.0f ? m_run * 0.69314718055994531f + logf(l_all) : -__builtin_inff();
+      a.lse[(int64_t)qi * a.Hq + head] = l_all > 0.0f ? m_use * 0.69314718055994531f + logf(l_all) : -__builtin_inff();
   } else {
     const int64_t slot = ((int64_t)qi * a.n_split + split) * a.Hq + head;
     float* op = a.part_o + slot * kAttnC;
 #pragma unroll
     for (int t = 0; t < 32; ++t)
       *reinterpret_cast<float4*>(op + 16 * t + 4 * g) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
-    if (g == 0) { a.part_ml[2 * slot] = m_run; a.part_ml[2 * slot + 1] = l_all; }
+    if (g == 0) { a.part_ml[2 * slot] = l_all > 0.0f ? m_use : -__builtin_inff(); a.part_ml[2 * slot + 1] = l_all; }
   }
 }
 
