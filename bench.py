@@ -14,7 +14,10 @@ One step = the whole hot path of the layer for the batch:
   fp4kv_index_select      (top-2,048 blocks -> pool -> top-512 tokens)
   fp4kv_sparse_attn_decode (FP4 gather-dequant attention + window + LSE merge)
 
-Prints one JSON line (see the README of the contract in the design doc).
+Prints one JSON line: the metric (queries/s), the step time, the roofline of
+the dominant kernel (the scan: algorithmic bytes per launch over its measured
+launch time, against 8 TB/s, with the HBM traffic the byte counters measured)
+and the float64 oracle's rate on the host cores as a CPU baseline.
 """
 from __future__ import annotations
 
@@ -139,7 +142,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the decode batch shards by query "
-              f"with no exchange; see DESIGN.md)", file=sys.stderr)
+              f"with no exchange: each GPU runs this same workload on its own queries)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -13,19 +13,21 @@
 // held in registers (a longer block list is re-read from global memory in
 // each pass instead). A selection of kk of the candidates is
 //   1. a radix search for the threshold key T: 8-bit digits from the highest
-//      bit where the candidates differ, per-wave histograms in LDS, bin totals
-//      summed by 256 threads, the bin that reaches rank kk found by one wave;
-//      it stops early when that bin holds exactly the keys still needed;
+//      bit where the candidates differ down to the lowest (bits common to all
+//      candidates cost no pass, and the first pass spreads over many bins);
+//      per pass, LDS atomics into one 256-bin histogram, then one wave reads
+//      and clears the bins, finds the bin that reaches rank kk with a
+//      DPP prefix sum and broadcasts it; the search stops early when that bin
+//      holds exactly the keys still needed;
 //   2. an ordered compaction: each run counts keys > T and == T; one
 //      block-wide prefix sum of both counts gives each run its output offset
 //      (the ties taken before a run are the lesser of the ties before it and
-//      the ties to take, since ties go to lower indices), and the run writes
-//      its selected ids in index order.
-// Keys bunch in a narrow range (block maxima share exponent bits), so the
-// digits start at the highest bit where candidates differ and stop at the
-// lowest: bits common to every candidate cost no pass, and the first pass
-// spreads the LDS atomics over many bins instead of one or two.
-// Nothing depends on the order of atomic updates: results are deterministic.
+//      the ties to take, since ties go to lower indices); the runs write their
+//      selected ids in index order into LDS, and the result is copied out with
+//      its -1 padding in one coalesced pass.
+// Wave-level scans and reductions use DPP row shifts and row broadcasts; the
+// block-level ones cost one barrier. Nothing depends on the order of atomic
+// updates: results are deterministic.
 #include "kernels.h"
 
 namespace fp4kv {
@@ -35,63 +37,36 @@ constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kKPT = 16;                     // keys per thread held in registers
 constexpr int kRegKeys = kSelThreads * kKPT; // 16384
 
-struct SelShared {
-  uint32_t hist[kSelWaves][256];
-  uint32_t tot[256];
-  int32_t pool[kRegKeys / 8];
-  int32_t scan[kSelWaves];
-  int32_t scan2[kSelWaves][2];
-  uint32_t red[kSelWaves][2];
-  uint32_t bc[4];
+struct alignas(16) SelShared {
+  uint32_t hist[256];                        // digit histogram, zero between passes
+  int32_t pool[kRegKeys / 8];                // selected blocks, ascending
+  int32_t out[kRegKeys];                     // selected positions, ascending
+  uint32_t red[kSelWaves][4];                // per-wave partial results
+  uint32_t bc[4];                            // broadcast of the chosen bin
 };
 
-// Exclusive prefix sum over the workgroup; also returns the total.
-__device__ __forceinline__ int block_exclusive_scan(SelShared& sh, int v, int& total) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == kWave - 1) sh.scan[wave] = x;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const int s = sh.scan[w];
-    before += w < wave ? s : 0;
-    all += s;
-  }
-  __syncthreads();
-  total = all;
-  return before + x - v;
+// Inclusive scan of x over the 64 lanes of a wave with a commutative,
+// associative op of identity `ident`: DPP row shifts by 1, 2, 4, 8 within each
+// 16-lane row, then row broadcasts of lane 15 and lane 31 across rows.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, uint32_t ident, Op op) {
+  const int id = (int)ident;
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x111, 0xF, 0xF, false));   // row_shr:1
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x112, 0xF, 0xF, false));   // row_shr:2
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x114, 0xF, 0xF, false));   // row_shr:4
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x118, 0xF, 0xF, false));   // row_shr:8
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x142, 0xA, 0xF, false));   // row_bcast:15
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  return x;
 }
-
-// Exclusive prefix sums of two values over the workgroup, with totals.
-__device__ __forceinline__ void block_exclusive_scan2(SelShared& sh, int a, int b, int& ea, int& eb, int& ta, int& tb) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  int x = a, y = b;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int u = __shfl_up(x, d), v = __shfl_up(y, d);
-    if (lane >= d) { x += u; y += v; }
-  }
-  if (lane == kWave - 1) { sh.scan2[wave][0] = x; sh.scan2[wave][1] = y; }
-  __syncthreads();
-  int bx = 0, by = 0, sx = 0, sy = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const int u = sh.scan2[w][0], v = sh.scan2[w][1];
-    if (w < wave) { bx += u; by += v; }
-    sx += u; sy += v;
-  }
-  __syncthreads();
-  ea = bx + x - a; eb = by + y - b; ta = sx; tb = sy;
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t x) {
+  return wave_incl_scan(x, 0u, [](uint32_t p, uint32_t q) { return p + q; });
 }
+__device__ __forceinline__ uint32_t lane63(uint32_t x) { return (uint32_t)__builtin_amdgcn_readlane((int)x, 63); }
 
 // Keys of the calling thread's run: either 16 registers or a global-memory run.
 struct RegKeys {
+  static constexpr int kRun = kKPT;
   uint32_t k[kKPT];
   template <typename F> __device__ __forceinline__ void each(F f) const {
 #pragma unroll
@@ -100,6 +75,7 @@ struct RegKeys {
 };
 
 struct GlobalKeys {        // block maxima of a long context, keys computed on the fly
+  static constexpr int kRun = 1 << 30;     // unbounded run length
   const float* bm;
   int64_t lo, hi;          // this thread's run [lo, hi)
   template <typename F> __device__ __forceinline__ void each(F f) const {
@@ -107,23 +83,30 @@ struct GlobalKeys {        // block maxima of a long context, keys computed on t
   }
 };
 
-// Threshold key T of a top-kk selection, and how many keys equal to T to take
-// (INT_MAX when every key equal to T is selected).
+// OR and AND of the candidate keys (key 0 is not a candidate) and the number
+// of candidates, over the workgroup.
 template <typename Keys>
-__device__ void radix_threshold(SelShared& sh, const Keys& keys, int kk, uint32_t& T, int& take_eq) {
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  uint32_t vor = 0, vand = 0xFFFFFFFFu;
-  keys.each([&](int, uint32_t v) { if (v) { vor |= v; vand &= v; } });
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    vor |= __shfl_xor(vor, d);
-    vand &= __shfl_xor(vand, d);
-  }
-  if (lane == 0) { sh.red[wave][0] = vor; sh.red[wave][1] = vand; }
+__device__ void candidate_summary(SelShared& sh, const Keys& keys, uint32_t& vor, uint32_t& vand, int& count) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  uint32_t o = 0, n = 0xFFFFFFFFu, c = 0;
+  keys.each([&](int, uint32_t v) { if (v) { o |= v; n &= v; ++c; } });
+  o = lane63(wave_incl_scan(o, 0u, [](uint32_t p, uint32_t q) { return p | q; }));
+  n = lane63(wave_incl_scan(n, 0xFFFFFFFFu, [](uint32_t p, uint32_t q) { return p & q; }));
+  c = lane63(wave_incl_add(c));
+  if (lane == 0) { sh.red[wave][0] = o; sh.red[wave][1] = n; sh.red[wave][2] = c; }
   __syncthreads();
-  vor = 0; vand = 0xFFFFFFFFu;
+  vor = 0; vand = 0xFFFFFFFFu; count = 0;
 #pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) { vor |= sh.red[w][0]; vand &= sh.red[w][1]; }
+  for (int w = 0; w < kSelWaves; ++w) { vor |= sh.red[w][0]; vand &= sh.red[w][1]; count += (int)sh.red[w][2]; }
+}
+
+// Threshold key T of a top-kk selection among the candidates, and how many
+// keys equal to T to take (INT_MAX when every key equal to T is selected).
+// sh.hist is zero on entry and on return.
+template <typename Keys>
+__device__ void radix_threshold(SelShared& sh, const Keys& keys, int kk, uint32_t vor, uint32_t vand, uint32_t& T,
+                                int& take_eq) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const uint32_t diff = vor ^ vand;
   if (diff == 0) { T = vand; take_eq = kk; __syncthreads(); return; }  // all candidates equal: the first kk
   // Only bits lo..hi differ between candidates: digits of up to 8 bits cover
@@ -138,39 +121,27 @@ __device__ void radix_threshold(SelShared& sh, const Keys& keys, int kk, uint32_
     const int shift = top - 7 > lo ? top - 7 : lo;
     const int width = top - shift + 1;
     const uint32_t dmask = (1u << width) - 1u;
-    for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&sh.hist[0][0])[i] = 0;
-    __syncthreads();
     keys.each([&](int, uint32_t v) {
-      if (v && (v & mask) == prefix) atomicAdd(&sh.hist[wave][(v >> shift) & dmask], 1u);
+      if (v && (v & mask) == prefix) atomicAdd(&sh.hist[(v >> shift) & dmask], 1u);
     });
     __syncthreads();
-    if (tid < 256) {
-      uint32_t t = 0;
-#pragma unroll
-      for (int w = 0; w < kSelWaves; ++w) t += sh.hist[w][tid];
-      sh.tot[tid] = t;
-    }
-    __syncthreads();
     if (wave == 0) {
-      // lane owns bins 4*lane .. 4*lane+3; counts from the top bin down
-      uint32_t c[4], t = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { c[j] = sh.tot[4 * lane + j]; t += c[j]; }
-      uint32_t incl = t;
-#pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t x = __shfl_down(incl, d);
-        if (lane + d < kWave) incl += x;
-      }
-      uint32_t run = incl - t;  // keys in bins above this lane's bins
+      // lane owns bins 4*lane .. 4*lane+3: reads and clears them
+      uint4* hp = reinterpret_cast<uint4*>(&sh.hist[4 * lane]);
+      const uint4 c = *hp;
+      *hp = make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t t = c.x + c.y + c.z + c.w;
+      const uint32_t incl = wave_incl_add(t);
+      uint32_t run = lane63(incl) - incl;     // keys in the bins above this lane's bins
+      const uint32_t cb[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
       for (int j = 3; j >= 0; --j) {
-        if (run < (uint32_t)kr && run + c[j] >= (uint32_t)kr) {
+        if (run < (uint32_t)kr && run + cb[j] >= (uint32_t)kr) {
           sh.bc[0] = (uint32_t)(4 * lane + j);
           sh.bc[1] = run;
-          sh.bc[2] = c[j];
+          sh.bc[2] = cb[j];
         }
-        run += c[j];
+        run += cb[j];
       }
     }
     __syncthreads();
@@ -184,7 +155,6 @@ __device__ void radix_threshold(SelShared& sh, const Keys& keys, int kk, uint32_
       break;
     }
   }
-  __syncthreads();
   // bits below the last digit: all candidates share them (common low bits)
   T = prefix | (vand & ~mask);
   if (take_eq < 0) take_eq = kr;
@@ -195,21 +165,44 @@ __device__ void radix_threshold(SelShared& sh, const Keys& keys, int kk, uint32_
 // min(ties before it, take_eq), because ties are taken from the lowest index.
 template <typename Keys, typename Out>
 __device__ int compact_selected(SelShared& sh, const Keys& keys, uint32_t T, int take_eq, Out out) {
-  int gt = 0, eq = 0;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  uint32_t gt = 0, eq = 0;
   keys.each([&](int, uint32_t v) { gt += v > T; eq += (v == T) & (v != 0u); });
-  int gt_total, eq_total;
-  int gt_before, eq_before;
-  block_exclusive_scan2(sh, gt, eq, gt_before, eq_before, gt_total, eq_total);
+  const uint32_t igt = wave_incl_add(gt), ieq = wave_incl_add(eq);
+  if (lane == 63) { sh.red[wave][0] = igt; sh.red[wave][1] = ieq; }
+  __syncthreads();
+  int gt_before = (int)(igt - gt), eq_before = (int)(ieq - eq), gt_total = 0, eq_total = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int u = (int)sh.red[w][0], v = (int)sh.red[w][1];
+    if (w < wave) { gt_before += u; eq_before += v; }
+    gt_total += u; eq_total += v;
+  }
   const int taken_before = min(eq_before, take_eq);
   int take = take_eq - eq_before;
-  take = take < 0 ? 0 : (take > eq ? eq : take);
+  take = take < 0 ? 0 : (take > (int)eq ? (int)eq : take);
   int slot = gt_before + taken_before;
   int taken = 0;
-  keys.each([&](int j, uint32_t v) {
-    bool sel = v > T;
-    if (!sel && v == T && v != 0u && taken < take) { sel = true; ++taken; }
-    if (sel) out(slot++, j);
-  });
+  if constexpr (Keys::kRun <= 32) {
+    // register run: collect the selected indices, then write only those
+    uint32_t selmask = 0;
+    keys.each([&](int j, uint32_t v) {
+      bool sel = v > T;
+      if (!sel && v == T && v != 0u && taken < take) { sel = true; ++taken; }
+      selmask |= (uint32_t)sel << j;
+    });
+    while (selmask) {
+      const int j = __builtin_ctz(selmask);
+      selmask &= selmask - 1u;
+      out(slot++, j);
+    }
+  } else {
+    keys.each([&](int j, uint32_t v) {
+      bool sel = v > T;
+      if (!sel && v == T && v != 0u && taken < take) { sel = true; ++taken; }
+      if (sel) out(slot++, j);
+    });
+  }
   return gt_total + min(eq_total, take_eq);
 }
 
@@ -217,6 +210,8 @@ template <bool REINDEX>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ SelShared sh;
   const int qi = blockIdx.x, tid = threadIdx.x;
+  // histograms start at zero (the first barrier comes before any count)
+  if (tid < 64) reinterpret_cast<uint4*>(sh.hist)[tid] = make_uint4(0u, 0u, 0u, 0u);
 
   const int64_t base = a.seq_start[qi / a.q_per_seq];
   int64_t p = a.q_pos[qi];
@@ -248,27 +243,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 #pragma unroll
         for (int j = 0; j < kKPT; ++j) keys.k[j] = i0 + j < nblk ? float_key(bm[i0 + j]) : 0u;
       }
-      uint32_t T; int take_eq;
-      radix_threshold(sh, keys, kk, T, take_eq);
-      npool = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) {
-        const int32_t b = (int32_t)(i0 + j);
-        sh.pool[slot] = b;
-        pool_row[slot] = b;
-      });
+      uint32_t vor, vand, T; int cnt, take_eq;
+      candidate_summary(sh, keys, vor, vand, cnt);
+      radix_threshold(sh, keys, kk, vor, vand, T, take_eq);
+      npool = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) { sh.pool[slot] = (int32_t)(i0 + j); });
     } else if (kk > 0) {
       const int64_t per = (nblk + kSelThreads - 1) / kSelThreads;
       GlobalKeys keys{bm, min<int64_t>((int64_t)tid * per, nblk), min<int64_t>((int64_t)tid * per + per, nblk)};
-      uint32_t T; int take_eq;
-      radix_threshold(sh, keys, kk, T, take_eq);
-      npool = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) {
-        const int32_t b = (int32_t)(keys.lo + j);
-        sh.pool[slot] = b;
-        pool_row[slot] = b;
-      });
+      uint32_t vor, vand, T; int cnt, take_eq;
+      candidate_summary(sh, keys, vor, vand, cnt);
+      radix_threshold(sh, keys, kk, vor, vand, T, take_eq);
+      npool = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) { sh.pool[slot] = (int32_t)(keys.lo + j); });
     }
-    for (int i = npool + tid; i < a.P; i += kSelThreads) pool_row[i] = -1;
-    if (tid == 0) a.n_pool[qi] = npool;
     __syncthreads();
+    for (int i = tid; i < a.P; i += kSelThreads) pool_row[i] = i < npool ? sh.pool[i] : -1;
+    if (tid == 0) a.n_pool[qi] = npool;
   } else {
     npool = a.n_pool[qi];
     npool = npool < 0 ? 0 : (npool > a.P ? a.P : npool);
@@ -279,7 +268,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   // ---- pool positions -> top-k. Candidate j (< npool*8) is position
   // pool[j/8]*8 + j%8; thread t owns candidates 16t .. 16t+15 (two blocks).
   RegKeys keys;
-  int nvalid_local = 0;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int jb = 2 * tid + half;                     // pool slot
@@ -303,23 +291,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     for (int e = 0; e < 8; ++e) {
       const bool ok = b >= 0 && b * 8 + e < n_vis;
       keys.k[8 * half + e] = ok ? float_key(s[e]) : 0u;
-      nvalid_local += ok;
     }
   }
-  int nvalid;
-  block_exclusive_scan(sh, nvalid_local, nvalid);
+  // float_key never gives 0 for a finite score, so the candidates are the visible positions
+  uint32_t vor, vand; int nvalid;
+  candidate_summary(sh, keys, vor, vand, nvalid);
   const int kk = min(a.k, nvalid);
   int32_t* out = a.idx_out + (int64_t)qi * a.k;
   int nsel = 0;
   if (kk > 0) {
     uint32_t T; int take_eq;
-    radix_threshold(sh, keys, kk, T, take_eq);
+    radix_threshold(sh, keys, kk, vor, vand, T, take_eq);
     nsel = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) {
-      const int jb = 2 * tid + (j >> 3);
-      out[slot] = sh.pool[jb] * 8 + (j & 7);
+      sh.out[slot] = sh.pool[2 * tid + (j >> 3)] * 8 + (j & 7);
     });
   }
-  for (int i = nsel + tid; i < a.k; i += kSelThreads) out[i] = -1;
+  __syncthreads();
+  for (int i = tid; i < a.k; i += kSelThreads) out[i] = i < nsel ? sh.out[i] : -1;
   if (tid == 0) a.n_idx[qi] = nsel;
 }
 
