@@ -10,8 +10,9 @@
 //
 // One 1024-thread workgroup per query. Scores map to order-preserving 32-bit
 // keys (0 = not a candidate). Each thread owns a contiguous run of 16 keys,
-// held in registers (a longer block list is re-read from global memory in
-// each pass instead). A selection of kk of the candidates is
+// held in registers. A longer block list is re-read from global memory in
+// each pass, in chunks of 16,384 keys where each thread again owns 16
+// consecutive keys (coalesced), and is compacted chunk by chunk. A selection of kk of the candidates is
 //   1. a radix search for the threshold key T: 8-bit digits from the highest
 //      bit where the candidates differ down to the lowest (bits common to all
 //      candidates cost no pass, and the first pass spreads over many bins);
@@ -74,12 +75,37 @@ struct RegKeys {
   }
 };
 
-struct GlobalKeys {        // block maxima of a long context, keys computed on the fly
-  static constexpr int kRun = 1 << 30;     // unbounded run length
+// Keys of the calling thread in one 16,384-key chunk of a longer block list:
+// 16 consecutive block maxima (coalesced across the wave), key 0 past the end.
+__device__ __forceinline__ void load_run(const float* bm, int64_t n, int64_t i0, uint32_t (&k)[kKPT]) {
+  if (i0 + kKPT <= n && (((uintptr_t)(bm + i0)) & 15) == 0) {
+    const float4* v = reinterpret_cast<const float4*>(bm + i0);
+#pragma unroll
+    for (int j = 0; j < kKPT / 4; ++j) {
+      const float4 f = v[j];
+      k[4 * j] = float_key(f.x); k[4 * j + 1] = float_key(f.y);
+      k[4 * j + 2] = float_key(f.z); k[4 * j + 3] = float_key(f.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kKPT; ++j) k[j] = i0 + j < n ? float_key(bm[i0 + j]) : 0u;
+  }
+}
+
+// Block maxima of a long context (more than 16,384 blocks), re-read from
+// global memory in each pass: chunk c of 16,384 keys gives thread t the run
+// c*16384 + 16t .. +15.
+struct GlobalKeys {
+  static constexpr int kRun = 1 << 30;     // no register run
   const float* bm;
-  int64_t lo, hi;          // this thread's run [lo, hi)
+  int64_t n;
   template <typename F> __device__ __forceinline__ void each(F f) const {
-    for (int64_t i = lo; i < hi; ++i) f((int)(i - lo), float_key(bm[i]));
+    for (int64_t c0 = 0; c0 < n; c0 += kRegKeys) {
+      uint32_t k[kKPT];
+      load_run(bm, n, c0 + (int64_t)threadIdx.x * kKPT, k);
+#pragma unroll
+      for (int j = 0; j < kKPT; ++j) f(j, k[j]);
+    }
   }
 };
 
@@ -206,6 +232,54 @@ __device__ int compact_selected(SelShared& sh, const Keys& keys, uint32_t T, int
   return gt_total + min(eq_total, take_eq);
 }
 
+// Ordered compaction of a long block list, chunk by chunk: within a chunk as
+// compact_selected; the ties taken so far and the slots filled so far carry
+// from one chunk to the next. out(slot, block id).
+template <typename Out>
+__device__ int compact_chunks(SelShared& sh, const GlobalKeys& keys, uint32_t T, int take_eq, Out out) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  int filled = 0, ties_left = take_eq;
+  for (int64_t c0 = 0; c0 < keys.n; c0 += kRegKeys) {
+    const int64_t i0 = c0 + (int64_t)threadIdx.x * kKPT;
+    uint32_t k[kKPT];
+    load_run(keys.bm, keys.n, i0, k);
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < kKPT; ++j) { gt += k[j] > T; eq += (k[j] == T) & (k[j] != 0u); }
+    const uint32_t igt = wave_incl_add(gt), ieq = wave_incl_add(eq);
+    if (lane == 63) { sh.red[wave][0] = igt; sh.red[wave][1] = ieq; }
+    __syncthreads();
+    int gt_before = (int)(igt - gt), eq_before = (int)(ieq - eq), gt_total = 0, eq_total = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+      const int u = (int)sh.red[w][0], v = (int)sh.red[w][1];
+      if (w < wave) { gt_before += u; eq_before += v; }
+      gt_total += u; eq_total += v;
+    }
+    __syncthreads();                         // sh.red is rewritten by the next chunk
+    const int ties_here = min(eq_total, ties_left);
+    int take = ties_here - eq_before;
+    take = take < 0 ? 0 : (take > (int)eq ? (int)eq : take);
+    int slot = filled + gt_before + min(eq_before, ties_here);
+    int taken = 0;
+    uint32_t selmask = 0;
+#pragma unroll
+    for (int j = 0; j < kKPT; ++j) {
+      bool sel = k[j] > T;
+      if (!sel && k[j] == T && k[j] != 0u && taken < take) { sel = true; ++taken; }
+      selmask |= (uint32_t)sel << j;
+    }
+    while (selmask) {
+      const int j = __builtin_ctz(selmask);
+      selmask &= selmask - 1u;
+      out(slot++, i0 + j);
+    }
+    filled += gt_total + ties_here;
+    ties_left -= ties_here;
+  }
+  return filled;
+}
+
 template <bool REINDEX>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ SelShared sh;
@@ -248,12 +322,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       radix_threshold(sh, keys, kk, vor, vand, T, take_eq);
       npool = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) { sh.pool[slot] = (int32_t)(i0 + j); });
     } else if (kk > 0) {
-      const int64_t per = (nblk + kSelThreads - 1) / kSelThreads;
-      GlobalKeys keys{bm, min<int64_t>((int64_t)tid * per, nblk), min<int64_t>((int64_t)tid * per + per, nblk)};
+      GlobalKeys keys{bm, nblk};
       uint32_t vor, vand, T; int cnt, take_eq;
       candidate_summary(sh, keys, vor, vand, cnt);
       radix_threshold(sh, keys, kk, vor, vand, T, take_eq);
-      npool = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) { sh.pool[slot] = (int32_t)(keys.lo + j); });
+      npool = compact_chunks(sh, keys, T, take_eq, [&](int slot, int64_t b) { sh.pool[slot] = (int32_t)b; });
     }
     __syncthreads();
     for (int i = tid; i < a.P; i += kSelThreads) pool_row[i] = i < npool ? sh.pool[i] : -1;

@@ -98,14 +98,29 @@ CONFIGS = {
                       Hq=64, ctx=131096, T=4096, pos0=127000),
     "mixed": Config("mixed", 4, "mixed", n_seq=64, H=16, D=128, qk=(-8, 8), wr=(1, 8), P=2048, k=512, Hq=64,
                     append_per_seq=1024),
+    # the prefill chunk through a Full group and a Reindex group of the decoder schedule
+    "prefill_chain": Config("prefill_chain", 5, "prefill", n_seq=1, H=16, D=128, qk=(-8, 8), wr=(1, 8), P=2048,
+                            k=512, Hq=64, ctx=131096, T=4096, pos0=127000,
+                            modes=("full", "reuse", "reuse", "reuse", "reindex", "reuse", "reuse", "reuse")),
+    # the 20 decoder layers (1 Full + 3 Reuse, then 4 x (1 Reindex + 3 Reuse)) at 1M context
+    "decoder1m": Config("decoder1m", 6, "chain", n_seq=4, H=16, D=128, qk=(-8, 8), wr=(1, 8), P=2048, k=512,
+                        Hq=64, ctx=2 ** 20,
+                        modes=("full", "reuse", "reuse", "reuse") + ("reindex", "reuse", "reuse", "reuse") * 4),
+    # the 18 encoder layers (3 x (1 Full + 5 Reuse)) over a 1,024-query chunk
+    "encoder_chunk": Config("encoder_chunk", 7, "prefill", n_seq=1, H=16, D=128, qk=(-8, 8), wr=(1, 8), P=2048,
+                            k=512, Hq=64, ctx=131072, T=1024, pos0=130048,
+                            modes=("full", "reuse", "reuse", "reuse", "reuse", "reuse") * 3),
 }
 
 # entity ids: sequences use their index; per-(layer, query) tensors use
-# (layer + 1) << 20 | query, so streams never collide.
+# (layer + 1) << 16 | query, so streams never collide. Counters are
+# entity << 40 | element, so entities stay below 2^23 (127 layers, 65,536 queries).
 
 
 def lq(layer: int, i: int) -> int:
-    return ((layer + 1) << 20) | i
+    if not (0 <= layer < 127 and 0 <= i < (1 << 16)):
+        raise ValueError(f"layer {layer} / query {i} outside the stream-id range")
+    return ((layer + 1) << 16) | i
 
 
 # ---- per-row generators (any device) ----------------------------------------

@@ -166,6 +166,20 @@ def test_index_full_all_equal_scores(fk, gpu):
     _indexer_case(fk, gpu, [5000, 9, 130], 8, 64, 16, 40, seed=23, lo=1, hi=1)
 
 
+def test_index_full_long_block_lists(fk, gpu):
+    """More than 16,384 blocks: the block maxima are re-read in chunks, with a
+    ragged last chunk, and the pool is compacted chunk by chunk."""
+    _say("index_full long block lists")
+    _indexer_case(fk, gpu, [140000, 300001, 5000], 4, 64, 2048, 512, seed=51)
+
+
+def test_index_full_long_block_lists_ties(fk, gpu):
+    """Heavy ties across chunks: ties go to the lowest block ids, so they are
+    taken from the first chunks in order."""
+    _say("index_full long block lists with ties")
+    _indexer_case(fk, gpu, [200000, 150001], 4, 64, 2048, 512, seed=53, lo=-1, hi=1)
+
+
 def test_index_full_prefill_positions(fk, gpu):
     """One sequence, many queries at consecutive positions (causal)."""
     _say("index_full prefill-style positions")
