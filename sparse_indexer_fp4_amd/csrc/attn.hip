@@ -20,45 +20,51 @@
 // against the old maximum (values up to 2^8, still exact after the hi/lo
 // split), so the 128 accumulators per lane are normally touched by MFMA only.
 //
-// Workgroup = (query, split); one wave per group of 16 heads. A split takes
-// every n_split-th 32-row chunk. Each chunk is dequantised once into LDS by
-// the whole workgroup, one (8 rows x 8 channels) item per thread: the codes of
-// a row are read as one coalesced 256-byte line per wave, E2M1 magnitudes come
-// from a byte table (v_perm), and the item is written as a row-major copy (the
-// K operand of S^T = K Q^T) and a channel-major copy (the V^T operand of
-// O^T = V^T P^T), both in 16-byte units placed to avoid bank conflicts. The
-// raw bytes of the next sparse chunk are loaded into registers while the
-// current one is computed. Chunk rows 2j and 2j+1 are the j-th rows of the two
-// 16-row MFMA tiles, so each lane's eight P values are exactly the eight rows
-// its P^T operand needs. With one split the result is written directly;
-// otherwise (m, l, O) partials go to the workspace and a combine kernel merges
-// them.
+// Workgroup = (query, split); two waves per group of 16 heads, each owning
+// half of the 512 output channels (64 accumulators per lane, so that two waves
+// fit on a SIMD and hide each other's LDS and MFMA latencies). Each wave forms
+// the partial S over its channel half; the two partials are exchanged through
+// LDS and added in the same order by both waves. A split takes every
+// n_split-th 32-row chunk. Each chunk is dequantised once into LDS by the whole
+// workgroup, one (4 rows x 8 channels) item per thread: the codes of a row are
+// read as one coalesced 256-byte line per wave, E2M1 magnitudes come from a
+// byte table (v_perm), and the item is written as a row-major copy (the K
+// operand of S^T = K Q^T) and a channel-major copy (the V^T operand of
+// O^T = V^T P^T), both padded so that the MFMA operand reads fall in distinct
+// bank groups. The raw bytes of the next sparse chunk are loaded into registers
+// while the current one is computed, and are not touched (masked) until the
+// chunk is committed, so the loads stay in flight. Chunk rows 2j and 2j+1 are
+// the j-th rows of the two 16-row MFMA tiles, so each lane's eight P values are
+// exactly the eight rows its P^T operand needs. With one split the result is
+// written directly; otherwise (m, l, O) partials go to the workspace and a
+// combine kernel merges them.
 #include "kernels.h"
 
 namespace fp4kv {
 
 constexpr int kAttnC = 512;       // channels (the kernels are written for 512)
 constexpr int kChunk = 32;        // rows per chunk
-constexpr int kItems = (kChunk / 8) * (kAttnC / 8);   // (8-row, 8-channel) items = 256
+constexpr int kItems = (kChunk / 4) * (kAttnC / 8);   // (4-row, 8-channel) items = 512
 
+constexpr int kKbufUnits = kChunk * 64 + kChunk / 2;          // 64 units per row + 1 per row pair
+constexpr int kVtUnits = kAttnC * 4 + kAttnC / 4;               // 4 units per channel + 1 per 4 channels
+
+template <int NHG>
 struct AttnShared {
-  uint4 kbuf[kChunk * kAttnC / 8];       // row-major bf16 in 16-byte units: 32 KB
-  uint4 vt[kAttnC * kChunk / 8];         // channel-major bf16, 8 rows per unit: 32 KB
-  uint32_t valid;                        // bit r: chunk row r is a real row
+  uint4 kbuf[kKbufUnits];                // row-major bf16 in 16-byte units: 33 KB
+  uint4 vt[kVtUnits];                    // channel-major bf16, 8 rows per unit: 34 KB
+  float sp[NHG][2][64][8];               // partial S of each head group's two channel halves
+  uint32_t vb[kChunk / 4];               // bit r of word q: chunk row 4q+r is a real row
 };
 
-// 16-byte unit holding channels 8u..8u+7 of chunk row `row`. Rows of equal
-// parity (one MFMA tile) spread over all 16 bank groups.
-__device__ __forceinline__ int kbuf_unit(int row, int u) { return row * 64 + (u ^ ((row >> 1) & 15)); }
-// 16-byte unit holding rows 8q..8q+7 of channel ch. Channels are permuted within
-// aligned groups of 4 and the row quarter is flipped, so that both the 8 channels
-// 8c+e (c = 0..7) written together and the 8 consecutive channels read together
-// land in distinct bank groups.
-__device__ __forceinline__ int vt_unit(int ch, int q) {
-  const int pc = ch ^ ((ch >> 3) & 3);
-  const int f = ((ch >> 2) ^ (ch >> 5)) & 1;
-  return pc * 4 + (q ^ f);
-}
+// 16-byte unit holding channels 8u..8u+7 of chunk row `row`. One unit of
+// padding per row pair: the 16 rows of equal parity read by one MFMA tile fall
+// in 16 distinct bank groups.
+__device__ __forceinline__ int kbuf_unit(int row, int u) { return row * 64 + (row >> 1) + u; }
+// 16-byte unit holding rows 8q..8q+7 of channel ch. One unit of padding per 4
+// channels: the 16 consecutive channels read by one MFMA tile fall in 16
+// distinct bank groups.
+__device__ __forceinline__ int vt_unit(int ch, int q) { return ch * 4 + (ch >> 2) + q; }
 
 // Half the value of an E4M3 scale code (sign bit never set): exact in fp32.
 __device__ __forceinline__ float e4m3_half(uint32_t c) {
@@ -72,10 +78,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Raw FP4 bytes of one item: channels 8c..8c+7 of 8 consecutive rows.
+// Raw FP4 bytes of one item: channels 8c..8c+7 of 4 consecutive rows.
 struct RawItem {
-  uint32_t code[8];   // 8 nibbles per row
-  uint32_t scale[8];  // the row's scale byte for these channels
+  uint32_t code[4];   // 8 nibbles per row (loaded from a stand-in row when the row is not real)
+  uint32_t scale[4];  // the row's scale byte for these channels (likewise)
+  uint32_t valid;     // bit r: row r is real; the others are zeroed when committed
 };
 
 struct QueryInfo {
@@ -109,63 +116,76 @@ __device__ __forceinline__ int64_t sparse_row(const AttnArgs& a, const QueryInfo
   return row < a.total_rows ? row : -1;
 }
 
-// Item `item` of a chunk: row group (8 rows) and channel group (8 channels).
+// Item `item` of a chunk: row group (4 rows) and channel group (8 channels).
 // Row groups are wave-uniform: a wave covers whole rows.
 __device__ __forceinline__ int item_rows(int item) { return __builtin_amdgcn_readfirstlane(item >> 6); }
 
 // Prefetch the raw bytes of sparse chunk c (window chunks are read at commit time).
-template <int NW>
+template <int NHG>
 __device__ __forceinline__ void load_chunk(const AttnArgs& a, const QueryInfo& Q, int qi, int c,
-                                           RawItem (&raw)[kItems / (64 * NW)]) {
-  constexpr int PER = kItems / (64 * NW);
+                                           RawItem (&raw)[kItems / (128 * NHG)]) {
+  constexpr int PER = kItems / (128 * NHG);
   if (c >= Q.cs) return;
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
-    const int item = threadIdx.x + it * 64 * NW;
+    const int item = threadIdx.x + it * 128 * NHG;
     const int rg = item_rows(item), cg = item & 63;
+    uint32_t bits = 0;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int64_t row = sparse_row(a, Q, qi, c * kChunk + 8 * rg + r);
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = sparse_row(a, Q, qi, c * kChunk + 4 * rg + r);
       const int64_t rr = row < 0 ? 0 : row;
-      const uint32_t code = *reinterpret_cast<const uint32_t*>(a.codes + rr * (kAttnC / 2) + 4 * cg);
-      const uint32_t sc = a.scales[rr * (kAttnC / 16) + (cg >> 1)];
-      raw[it].code[r] = row < 0 ? 0u : code;
-      raw[it].scale[r] = row < 0 ? 0u : sc;
+      // the loaded values are not touched until the chunk is committed, so
+      // the loads stay in flight while the current chunk is computed
+      raw[it].code[r] = *reinterpret_cast<const uint32_t*>(a.codes + rr * (kAttnC / 2) + 4 * cg);
+      raw[it].scale[r] = a.scales[rr * (kAttnC / 16) + (cg >> 1)];
+      bits |= (uint32_t)(row >= 0) << r;
+    }
+    raw[it].valid = bits;
+  }
+}
+
+// Write one item (4 rows x 8 channels as bf16 pairs d[row][pair]): the rows
+// into the row-major copy, and per channel the 4 rows as half of a unit of the
+// channel-major copy.
+template <int NHG>
+__device__ __forceinline__ void store_item(AttnShared<NHG>& sh, int rg, int cg, const uint32_t (&d)[4][4], bool keys,
+                                           bool values) {
+  if (keys) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sh.kbuf[kbuf_unit(4 * rg + r, cg)] = make_uint4(d[r][0], d[r][1], d[r][2], d[r][3]);
+  }
+  if (values) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high / low bf16 of each pair
+      const uint32_t w0 = __builtin_amdgcn_perm(d[1][e >> 1], d[0][e >> 1], sel);
+      const uint32_t w1 = __builtin_amdgcn_perm(d[3][e >> 1], d[2][e >> 1], sel);
+      uint2* u = reinterpret_cast<uint2*>(&sh.vt[vt_unit(8 * cg + e, rg >> 1)]);
+      u[rg & 1] = make_uint2(w0, w1);
     }
   }
 }
 
-// Write one item (8 rows x 8 channels as bf16 pairs d[row][pair]) into both copies.
-__device__ __forceinline__ void store_item(AttnShared& sh, int rg, int cg, const uint32_t (&d)[8][4]) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) sh.kbuf[kbuf_unit(8 * rg + r, cg)] = make_uint4(d[r][0], d[r][1], d[r][2], d[r][3]);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high / low bf16 of each pair
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_perm(d[2 * i + 1][e >> 1], d[2 * i][e >> 1], sel);
-    sh.vt[vt_unit(8 * cg + e, rg)] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-template <int NW>
-__device__ __forceinline__ void commit_chunk(AttnShared& sh, const QueryInfo& Q, const AttnArgs& a, int qi, int c,
-                                             const RawItem (&raw)[kItems / (64 * NW)]) {
-  constexpr int PER = kItems / (64 * NW);
+template <int NHG>
+__device__ __forceinline__ void commit_chunk(AttnShared<NHG>& sh, const QueryInfo& Q, const AttnArgs& a, int c,
+                                             const RawItem (&raw)[kItems / (128 * NHG)]) {
+  constexpr int PER = kItems / (128 * NHG);
   const bool sparse = c < Q.cs;
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
-    const int item = threadIdx.x + it * 64 * NW;
+    const int item = threadIdx.x + it * 128 * NHG;
     const int rg = item_rows(item), cg = item & 63;
-    uint32_t d[8][4];
+    uint32_t d[4][4];
     if (sparse) {
+      if (cg == 0) sh.vb[rg] = raw[it].valid;
       // twice the E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 as bytes
       constexpr uint32_t lut_lo = 0x03020100u, lut_hi = 0x0C080604u;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const uint32_t code = raw[it].code[r];
-        const float sh2 = e4m3_half(raw[it].scale[r]);
+      for (int r = 0; r < 4; ++r) {
+        const bool real = (raw[it].valid >> r) & 1u;
+        const uint32_t code = real ? raw[it].code[r] : 0u;
+        const float sh2 = e4m3_half(real ? raw[it].scale[r] : 0u);
         const uint32_t me = __builtin_amdgcn_perm(lut_hi, lut_lo, code & 0x07070707u);         // even channels
         const uint32_t mo = __builtin_amdgcn_perm(lut_hi, lut_lo, (code >> 4) & 0x07070707u);  // odd channels
 #pragma unroll
@@ -178,99 +198,100 @@ __device__ __forceinline__ void commit_chunk(AttnShared& sh, const QueryInfo& Q,
           d[r][j] = pack_bf16x2(f0, f1);
         }
       }
+      store_item<NHG>(sh, rg, cg, d, true, true);
     } else {
+      uint32_t bits = 0;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int wr = (c - Q.cs) * kChunk + 8 * rg + r;
+      for (int r = 0; r < 4; ++r) {
+        const int wr = (c - Q.cs) * kChunk + 4 * rg + r;
         const bool ok = wr < Q.n_w;
+        bits |= (uint32_t)ok << r;
         const int64_t row = Q.win_row0 + (ok ? wr : 0);
         const uint4 kv = ok ? *reinterpret_cast<const uint4*>(a.swa_k + row * kAttnC + 8 * cg) : make_uint4(0, 0, 0, 0);
         d[r][0] = kv.x; d[r][1] = kv.y; d[r][2] = kv.z; d[r][3] = kv.w;
       }
-      // keys: row-major copy only
+      if (cg == 0) sh.vb[rg] = bits;
+      store_item<NHG>(sh, rg, cg, d, true, false);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) sh.kbuf[kbuf_unit(8 * rg + r, cg)] = make_uint4(d[r][0], d[r][1], d[r][2], d[r][3]);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int wr = (c - Q.cs) * kChunk + 8 * rg + r;
+      for (int r = 0; r < 4; ++r) {
+        const int wr = (c - Q.cs) * kChunk + 4 * rg + r;
         const bool ok = wr < Q.n_w;
         const int64_t row = Q.win_row0 + (ok ? wr : 0);
         const uint4 vv = ok ? *reinterpret_cast<const uint4*>(a.swa_v + row * kAttnC + 8 * cg) : make_uint4(0, 0, 0, 0);
         d[r][0] = vv.x; d[r][1] = vv.y; d[r][2] = vv.z; d[r][3] = vv.w;
       }
-      // values: channel-major copy only
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_perm(d[2 * i + 1][e >> 1], d[2 * i][e >> 1], sel);
-        sh.vt[vt_unit(8 * cg + e, rg)] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-      continue;
+      store_item<NHG>(sh, rg, cg, d, false, true);
     }
-    store_item(sh, rg, cg, d);
-  }
-  if (threadIdx.x < 64) {
-    const int r = threadIdx.x;
-    bool ok = false;
-    if (r < kChunk) {
-      if (sparse) ok = sparse_row(a, Q, qi, c * kChunk + r) >= 0;
-      else ok = (c - Q.cs) * kChunk + r < Q.n_w;
-    }
-    const uint64_t b = __ballot(ok);
-    if (r == 0) sh.valid = (uint32_t)b;
   }
 }
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
-  constexpr int PER = kItems / (64 * NW);
-  __shared__ AttnShared sh;
+// Workgroup = (query, split): two waves per group of 16 heads, each owning half
+// of the 512 output channels (64 accumulators per lane, so two waves fit on a
+// SIMD). The two waves of a head group each form S over their half of the
+// channels and exchange the partial sums through LDS.
+template <int NHG>
+__global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
+  constexpr int PER = kItems / (128 * NHG);
+  __shared__ AttnShared<NHG> sh;
   const int split = blockIdx.x, qi = blockIdx.y;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int hg = wave >> 1, hc = wave & 1;          // head group, channel half
   const int g = lane / 16, hcol = lane % 16;
-  const int head = wave * 16 + hcol;
+  const int head = hg * 16 + hcol;
   const QueryInfo Q = query_info(a, qi);
   const int nchunk = Q.cs + Q.cw;
 
-  // Q^T operand: lane holds Q[head][32kk + 8g .. +7] for kk = 0..15
-  uint4 qv[16];
-  const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.Hq + head) * kAttnC);
+  // Q^T operand over this wave's channel half: lane holds Q[head][256hc + 32kk + 8g .. +7]
+  uint4 qv[8];
+  const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)qi * a.Hq + head) * kAttnC + 256 * hc);
 #pragma unroll
-  for (int kk = 0; kk < 16; ++kk) qv[kk] = qp[4 * kk + g];
+  for (int kk = 0; kk < 8; ++kk) qv[kk] = qp[4 * kk + g];
 
-  v4f o[32];
+  v4f o[16];
 #pragma unroll
-  for (int t = 0; t < 32; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 16; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_use = -__builtin_inff(), l_run = 0.0f;   // P is formed as exp2(x - m_use)
 
   RawItem raw[PER];
   int c = split;
-  if (c < nchunk) load_chunk<NW>(a, Q, qi, c, raw);
+  if (c < nchunk) load_chunk<NHG>(a, Q, qi, c, raw);
   for (; c < nchunk; c += a.n_split) {
     __syncthreads();
-    commit_chunk<NW>(sh, Q, a, qi, c, raw);
+    commit_chunk<NHG>(sh, Q, a, c, raw);
     __syncthreads();
-    if (c + a.n_split < nchunk) load_chunk<NW>(a, Q, qi, c + a.n_split, raw);
+    if (c + a.n_split < nchunk) load_chunk<NHG>(a, Q, qi, c + a.n_split, raw);
 
-    // S^T tiles: A = even rows (tile 0) / odd rows (tile 1), B = Q^T
+    // partial S^T over this channel half: A = even rows (tile 0) / odd rows (tile 1), B = Q^T
     v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const uint4 k0 = sh.kbuf[kbuf_unit(2 * hcol, 4 * kk + g)];
-      const uint4 k1 = sh.kbuf[kbuf_unit(2 * hcol + 1, 4 * kk + g)];
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint4 k0 = sh.kbuf[kbuf_unit(2 * hcol, 32 * hc + 4 * kk + g)];
+      const uint4 k1 = sh.kbuf[kbuf_unit(2 * hcol + 1, 32 * hc + 4 * kk + g)];
       const v8bf b = __builtin_bit_cast(v8bf, qv[kk]);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, k0), b, s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, k1), b, s1, 0, 0, 0);
     }
-    // lane holds rows 8g+2i (s0[i]) and 8g+2i+1 (s1[i]) for its head
-    const uint32_t valid = sh.valid;
+    {
+      float4* mine = reinterpret_cast<float4*>(&sh.sp[hg][hc][lane][0]);
+      mine[0] = make_float4(s0[0], s0[1], s0[2], s0[3]);
+      mine[1] = make_float4(s1[0], s1[1], s1[2], s1[3]);
+    }
+    __syncthreads();
+    // full S: the two halves added in the same order in both waves
+    const float4* h0 = reinterpret_cast<const float4*>(&sh.sp[hg][0][lane][0]);
+    const float4* h1 = reinterpret_cast<const float4*>(&sh.sp[hg][1][lane][0]);
+    const float4 a0 = h0[0], a1 = h0[1], b0 = h1[0], b1 = h1[1];
+    const float sa[4] = {a0.x + b0.x, a0.y + b0.y, a0.z + b0.z, a0.w + b0.w};
+    const float sb[4] = {a1.x + b1.x, a1.y + b1.y, a1.z + b1.z, a1.w + b1.w};
+    // lane holds rows 8g+2i (sa[i]) and 8g+2i+1 (sb[i]) for its head
+    uint32_t valid = 0;
+#pragma unroll
+    for (int q = 0; q < kChunk / 4; ++q) valid |= sh.vb[q] << (4 * q);
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[2 * i] = ((valid >> (8 * g + 2 * i)) & 1u) ? s0[i] * a.scale_log2 : -__builtin_inff();
-      x[2 * i + 1] = ((valid >> (8 * g + 2 * i + 1)) & 1u) ? s1[i] * a.scale_log2 : -__builtin_inff();
+      x[2 * i] = ((valid >> (8 * g + 2 * i)) & 1u) ? sa[i] * a.scale_log2 : -__builtin_inff();
+      x[2 * i + 1] = ((valid >> (8 * g + 2 * i + 1)) & 1u) ? sb[i] * a.scale_log2 : -__builtin_inff();
     }
     float cm = x[0];
 #pragma unroll
@@ -285,7 +306,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
       if (move) m_use = cm;
       l_run *= corr;
 #pragma unroll
-      for (int t = 0; t < 32; ++t) o[t] *= corr;
+      for (int t = 0; t < 16; ++t) o[t] *= corr;
     }
     float p[8], psum = 0.0f;
 #pragma unroll
@@ -299,31 +320,31 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
       plo[i] = (__bf16)(p[i] - (float)h);
     }
 #pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      const uint4 vtile = sh.vt[vt_unit(16 * t + hcol, g)];
+    for (int t = 0; t < 16; ++t) {
+      const uint4 vtile = sh.vt[vt_unit(256 * hc + 16 * t + hcol, g)];
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, vtile), phi, o[t], 0, 0, 0);
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, vtile), plo, o[t], 0, 0, 0);
     }
   }
 
-  // lane holds O^T[ch = 16t + 4g + i][head]; l_run is this lane's share of the sum
+  // lane holds O^T[ch = 256hc + 16t + 4g + i][head]; l_run is this lane's share of the sum
   float l_all = l_run + __shfl_xor(l_run, 16);
   l_all += __shfl_xor(l_all, 32);
   if (a.n_split == 1) {
     const float inv = l_all > 0.0f ? 1.0f / l_all : 0.0f;
-    float* op = a.out + ((int64_t)qi * a.Hq + head) * kAttnC;
+    float* op = a.out + ((int64_t)qi * a.Hq + head) * kAttnC + 256 * hc;
 #pragma unroll
-    for (int t = 0; t < 32; ++t)
+    for (int t = 0; t < 16; ++t)
       *reinterpret_cast<float4*>(op + 16 * t + 4 * g) = make_float4(o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv);
-    if (a.lse && g == 0)
+    if (a.lse && g == 0 && hc == 0)
       a.lse[(int64_t)qi * a.Hq + head] = l_all > 0.0f ? m_use * 0.69314718055994531f + logf(l_all) : -__builtin_inff();
   } else {
     const int64_t slot = ((int64_t)qi * a.n_split + split) * a.Hq + head;
-    float* op = a.part_o + slot * kAttnC;
+    float* op = a.part_o + slot * kAttnC + 256 * hc;
 #pragma unroll
-    for (int t = 0; t < 32; ++t)
+    for (int t = 0; t < 16; ++t)
       *reinterpret_cast<float4*>(op + 16 * t + 4 * g) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
-    if (g == 0) { a.part_ml[2 * slot] = l_all > 0.0f ? m_use : -__builtin_inff(); a.part_ml[2 * slot + 1] = l_all; }
+    if (g == 0 && hc == 0) { a.part_ml[2 * slot] = l_all > 0.0f ? m_use : -__builtin_inff(); a.part_ml[2 * slot + 1] = l_all; }
   }
 }
 
@@ -373,12 +394,12 @@ hipError_t launch_attn(AttnArgs a, void* ws, hipStream_t stream) {
     a.part_o = static_cast<float*>(ws);
     a.part_ml = a.part_o + (size_t)a.nq * a.n_split * a.Hq * kAttnC;
   }
-  const int nw = a.Hq / 16;
+  const int nhg = a.Hq / 16;
   dim3 grid((uint32_t)a.n_split, (uint32_t)a.nq);
-  switch (nw) {
-    case 1: attn_kernel<1><<<grid, dim3(64), 0, stream>>>(a); break;
-    case 2: attn_kernel<2><<<grid, dim3(128), 0, stream>>>(a); break;
-    case 4: attn_kernel<4><<<grid, dim3(256), 0, stream>>>(a); break;
+  switch (nhg) {
+    case 1: attn_kernel<1><<<grid, dim3(128), 0, stream>>>(a); break;
+    case 2: attn_kernel<2><<<grid, dim3(256), 0, stream>>>(a); break;
+    case 4: attn_kernel<4><<<grid, dim3(512), 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
