@@ -235,6 +235,8 @@ size_t fp4kv_attn_workspace_bytes(int32_t n_q, int32_t Hq, int32_t C, int32_t k,
  *   q          (device) bf16 [B, Hq, C]
  *   codes      (device) uint8 [total_rows, C/2]; scales (device) uint8 [total_rows, C/16]
  *   seq_start  (device) int64 [B]: first main-KV row of each query's sequence.
+ *   Alignment: q, swa_k, swa_v and out 16 bytes, codes 8 bytes, scales 4 bytes
+ *     (FP4KV_ERR_SHAPE otherwise).
  *   idx        (device) int32 [B, k]; n_idx (device) int32 [B]
  *   swa_k, swa_v (device) bf16 [B, W, C]
  *   q_pos      (device) int32 [B]

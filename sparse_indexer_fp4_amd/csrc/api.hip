@@ -264,8 +264,9 @@ static fp4kv_status check_attn(const char* fn, const void* q, const uint8_t* cod
   if (C != 512) return fail(FP4KV_ERR_UNSUPPORTED, "%s: C=%d (only 512 implemented)", fn, C);
   if (!std::isfinite(scale)) return fail(FP4KV_ERR_SHAPE, "%s: scale must be finite", fn);
   if (!aligned16(q) || !aligned16(swa_k) || !aligned16(swa_v) || !aligned16(out) ||
-      (reinterpret_cast<uintptr_t>(codes) & 7u))
-    return fail(FP4KV_ERR_SHAPE, "%s: q, swa_k, swa_v, out must be 16-byte and codes 8-byte aligned", fn);
+      (reinterpret_cast<uintptr_t>(codes) & 7u) || (reinterpret_cast<uintptr_t>(scales) & 3u))
+    return fail(FP4KV_ERR_SHAPE, "%s: q, swa_k, swa_v, out must be 16-byte, codes 8-byte and scales 4-byte aligned",
+                fn);
   const size_t need = fp4kv_attn_workspace_bytes(nq, Hq, C, k, W);
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(FP4KV_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu required", fn, ws_bytes, need);

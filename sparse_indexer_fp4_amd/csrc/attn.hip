@@ -25,19 +25,22 @@
 // fit on a SIMD and hide each other's LDS and MFMA latencies). Each wave forms
 // the partial S over its channel half; the two partials are exchanged through
 // LDS and added in the same order by both waves. A split takes every
-// n_split-th 32-row chunk. Each chunk is dequantised once into LDS by the whole
-// workgroup, one (4 rows x 8 channels) item per thread: the codes of a row are
-// read as one coalesced 256-byte line per wave, E2M1 magnitudes come from a
-// byte table (v_perm), and the item is written as a row-major copy (the K
-// operand of S^T = K Q^T) and a channel-major copy (the V^T operand of
-// O^T = V^T P^T), both padded so that the MFMA operand reads fall in distinct
-// bank groups. The raw bytes of the next sparse chunk are loaded into registers
-// while the current one is computed, and are not touched (masked) until the
-// chunk is committed, so the loads stay in flight. Chunk rows 2j and 2j+1 are
-// the j-th rows of the two 16-row MFMA tiles, so each lane's eight P values are
-// exactly the eight rows its P^T operand needs. With one split the result is
-// written directly; otherwise (m, l, O) partials go to the workspace and a
-// combine kernel merges them.
+// n_split-th 32-row chunk, its first window chunk first. Each chunk is
+// dequantised once into LDS by the whole workgroup, one (4 rows x 8 channels)
+// item per thread: the codes of a row are read as one coalesced 256-byte line
+// per wave and E2M1 magnitudes come from a byte table (v_perm). Rows are stored
+// row-major only, with an XOR swizzle of the 16-byte units that keeps the S
+// reads, the P V reads and the commit writes free of bank conflicts; the V^T
+// operand of O^T = V^T P^T is read from the same rows with the LDS transposing
+// read (ds_read_b64_tr_b16), so no channel-major copy is made. Window values
+// (which differ from their keys) get a second row-major buffer. The selected
+// positions a split needs are read with one vector load at the start; the raw
+// bytes of the next sparse chunk are loaded into registers while the current
+// one is computed and are not touched until it is committed, so the loads stay
+// in flight. Chunk rows 2j and 2j+1 are the j-th rows of the two 16-row MFMA
+// tiles, so each lane's eight P values are exactly the eight rows its P^T
+// operand needs. With one split the result is written directly; otherwise
+// (m, l, O) partials go to the workspace and a combine kernel merges them.
 #include "kernels.h"
 
 namespace fp4kv {
@@ -46,25 +49,26 @@ constexpr int kAttnC = 512;       // channels (the kernels are written for 512)
 constexpr int kChunk = 32;        // rows per chunk
 constexpr int kItems = (kChunk / 4) * (kAttnC / 8);   // (4-row, 8-channel) items = 512
 
-constexpr int kKbufUnits = kChunk * 64 + kChunk / 2;          // 64 units per row + 1 per row pair
-constexpr int kVtUnits = kAttnC * 4 + kAttnC / 4;               // 4 units per channel + 1 per 4 channels
+constexpr int kRowUnits = kChunk * 64;   // a chunk's rows in 16-byte units (64 per row)
 
 template <int NHG>
 struct AttnShared {
-  uint4 kbuf[kKbufUnits];                // row-major bf16 in 16-byte units: 33 KB
-  uint4 vt[kVtUnits];                    // channel-major bf16, 8 rows per unit: 34 KB
+  uint4 kbuf[kRowUnits];                 // row-major bf16 keys (= values for sparse rows): 32 KB
+  uint4 vbuf[kRowUnits];                 // row-major bf16 values of a window chunk: 32 KB
   float sp[NHG][2][64][8];               // partial S of each head group's two channel halves
   uint32_t vb[kChunk / 4];               // bit r of word q: chunk row 4q+r is a real row
 };
 
-// 16-byte unit holding channels 8u..8u+7 of chunk row `row`. One unit of
-// padding per row pair: the 16 rows of equal parity read by one MFMA tile fall
-// in 16 distinct bank groups.
-__device__ __forceinline__ int kbuf_unit(int row, int u) { return row * 64 + (row >> 1) + u; }
-// 16-byte unit holding rows 8q..8q+7 of channel ch. One unit of padding per 4
-// channels: the 16 consecutive channels read by one MFMA tile fall in 16
-// distinct bank groups.
-__device__ __forceinline__ int vt_unit(int ch, int q) { return ch * 4 + (ch >> 2) + q; }
+// 16-byte unit holding channels 8u..8u+7 of chunk row `row`: the unit index is
+// XOR-swizzled by a function of the row bits r0..r4, x = r2 | r1 << 1 |
+// (r0 ^ r3) << 2 | (r0 ^ r4) << 3. With it the three access patterns fall in
+// distinct LDS banks: the K-operand reads of S (16 rows of one parity, one
+// unit column), the transposing V-operand reads of P V (4 consecutive rows x
+// 32 bytes per 16 lanes, 8 rows per 32 lanes), and the row writes of a commit.
+__device__ __forceinline__ int row_swizzle(int row) {
+  return ((row >> 2) & 1) | (row & 2) | ((((row) ^ (row >> 3)) & 1) << 2) | ((((row) ^ (row >> 4)) & 1) << 3);
+}
+__device__ __forceinline__ int kbuf_unit(int row, int u) { return row * 64 + (u ^ row_swizzle(row)); }
 
 // Half the value of an E4M3 scale code (sign bit never set): exact in fp32.
 __device__ __forceinline__ float e4m3_half(uint32_t c) {
@@ -78,11 +82,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Raw FP4 bytes of one item: channels 8c..8c+7 of 4 consecutive rows.
-struct RawItem {
-  uint32_t code[4];   // 8 nibbles per row (loaded from a stand-in row when the row is not real)
-  uint32_t scale[4];  // the row's scale byte for these channels (likewise)
+// Raw bytes of one item, loaded one chunk ahead of its use. Sparse and
+// window chunks have register slots of their own, so that no slot ever holds
+// both kinds (merging the two would copy registers that are still being
+// loaded, which waits for the loads).
+struct RawSparse {
+  uint32_t code[4];   // channels 8c..8c+7 of row r (a stand-in row where row r is not real)
+  uint32_t scale[4];  // the row's aligned scale word holding these channels' scale byte (likewise)
   uint32_t valid;     // bit r: row r is real; the others are zeroed when committed
+};
+struct RawWindow {
+  uint4 k[4], v[4];   // bf16 keys and values, channels 8c..8c+7 of row r
+  uint32_t valid;
 };
 
 struct QueryInfo {
@@ -107,11 +118,10 @@ __device__ __forceinline__ QueryInfo query_info(const AttnArgs& a, int qi) {
   return r;
 }
 
-// Main-KV row of sparse slot j, or -1 if the slot is not a usable row.
-__device__ __forceinline__ int64_t sparse_row(const AttnArgs& a, const QueryInfo& qi_, int qi, int j) {
-  if (j >= qi_.n_s) return -1;
-  int64_t pos = a.idx[(int64_t)qi * a.k + j];
-  if (pos < 0 || pos > qi_.p) return -1;
+// Main-KV row of sparse slot j holding position `pos`, or -1 if the slot is
+// not a usable row.
+__device__ __forceinline__ int64_t sparse_row(const AttnArgs& a, const QueryInfo& qi_, int j, int64_t pos) {
+  if (j >= qi_.n_s || pos < 0 || pos > qi_.p) return -1;
   int64_t row = qi_.kv_base + pos;
   return row < a.total_rows ? row : -1;
 }
@@ -120,12 +130,35 @@ __device__ __forceinline__ int64_t sparse_row(const AttnArgs& a, const QueryInfo
 // Row groups are wave-uniform: a wave covers whole rows.
 __device__ __forceinline__ int item_rows(int item) { return __builtin_amdgcn_readfirstlane(item >> 6); }
 
-// Prefetch the raw bytes of sparse chunk c (window chunks are read at commit time).
+// The selected positions a wave needs are read with one vector load when the
+// workgroup starts: lane l holds the position of row 4*rg + (l & 3) of the
+// m-th chunk of this split, where m = l / (4 PER) and rg is the row group of the
+// wave's item (l / 4) % PER. Chunks past the 16/PER covered read their
+// positions directly.
 template <int NHG>
-__device__ __forceinline__ void load_chunk(const AttnArgs& a, const QueryInfo& Q, int qi, int c,
-                                           RawItem (&raw)[kItems / (128 * NHG)]) {
+__device__ __forceinline__ int idx_lane_load(const AttnArgs& a, int qi, int split, int lane) {
   constexpr int PER = kItems / (128 * NHG);
-  if (c >= Q.cs) return;
+  const int m = lane / (4 * PER), it = (lane / 4) % PER, r = lane & 3;
+  const int rg = (int)(threadIdx.x >> 6) + it * 2 * NHG;   // item_rows of item threadIdx.x + it * 128 * NHG
+  const int j = (split + m * a.n_split) * kChunk + 4 * rg + r;
+  return j < a.k ? a.idx[(int64_t)qi * a.k + j] : -1;
+}
+
+template <int NHG>
+__device__ __forceinline__ int64_t chunk_pos(const AttnArgs& a, int qi, int m, int j, int it, int r, int idxv) {
+  constexpr int PER = kItems / (128 * NHG);
+  if (m < 16 / PER) return __builtin_amdgcn_readlane(idxv, (m * PER + it) * 4 + r);
+  return j < a.k ? a.idx[(int64_t)qi * a.k + j] : -1;
+}
+
+// Issue the loads of chunk c, the m-th chunk of this split: FP4 codes and
+// scales of a sparse chunk, or bf16 keys and values of a window chunk. The
+// registers are not read until the chunk is committed, so the loads stay in
+// flight while the current chunk is computed.
+template <int NHG>
+__device__ __forceinline__ void load_sparse(const AttnArgs& a, const QueryInfo& Q, int qi, int c, int m, int idxv,
+                                            RawSparse (&raw)[kItems / (128 * NHG)]) {
+  constexpr int PER = kItems / (128 * NHG);
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
     const int item = threadIdx.x + it * 128 * NHG;
@@ -133,95 +166,101 @@ __device__ __forceinline__ void load_chunk(const AttnArgs& a, const QueryInfo& Q
     uint32_t bits = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t row = sparse_row(a, Q, qi, c * kChunk + 4 * rg + r);
+      const int j = c * kChunk + 4 * rg + r;
+      const int64_t row = sparse_row(a, Q, j, chunk_pos<NHG>(a, qi, m, j, it, r, idxv));
       const int64_t rr = row < 0 ? 0 : row;
-      // the loaded values are not touched until the chunk is committed, so
-      // the loads stay in flight while the current chunk is computed
       raw[it].code[r] = *reinterpret_cast<const uint32_t*>(a.codes + rr * (kAttnC / 2) + 4 * cg);
-      raw[it].scale[r] = a.scales[rr * (kAttnC / 16) + (cg >> 1)];
+      raw[it].scale[r] = *reinterpret_cast<const uint32_t*>(a.scales + rr * (kAttnC / 16) + 4 * (cg >> 3));
       bits |= (uint32_t)(row >= 0) << r;
     }
     raw[it].valid = bits;
   }
 }
 
-// Write one item (4 rows x 8 channels as bf16 pairs d[row][pair]): the rows
-// into the row-major copy, and per channel the 4 rows as half of a unit of the
-// channel-major copy.
 template <int NHG>
-__device__ __forceinline__ void store_item(AttnShared<NHG>& sh, int rg, int cg, const uint32_t (&d)[4][4], bool keys,
-                                           bool values) {
-  if (keys) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sh.kbuf[kbuf_unit(4 * rg + r, cg)] = make_uint4(d[r][0], d[r][1], d[r][2], d[r][3]);
-  }
-  if (values) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high / low bf16 of each pair
-      const uint32_t w0 = __builtin_amdgcn_perm(d[1][e >> 1], d[0][e >> 1], sel);
-      const uint32_t w1 = __builtin_amdgcn_perm(d[3][e >> 1], d[2][e >> 1], sel);
-      uint2* u = reinterpret_cast<uint2*>(&sh.vt[vt_unit(8 * cg + e, rg >> 1)]);
-      u[rg & 1] = make_uint2(w0, w1);
-    }
-  }
-}
-
-template <int NHG>
-__device__ __forceinline__ void commit_chunk(AttnShared<NHG>& sh, const QueryInfo& Q, const AttnArgs& a, int c,
-                                             const RawItem (&raw)[kItems / (128 * NHG)]) {
+__device__ __forceinline__ void load_window(const AttnArgs& a, const QueryInfo& Q, int c,
+                                            RawWindow (&raw)[kItems / (128 * NHG)]) {
   constexpr int PER = kItems / (128 * NHG);
-  const bool sparse = c < Q.cs;
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
     const int item = threadIdx.x + it * 128 * NHG;
     const int rg = item_rows(item), cg = item & 63;
-    uint32_t d[4][4];
-    if (sparse) {
-      if (cg == 0) sh.vb[rg] = raw[it].valid;
-      // twice the E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 as bytes
-      constexpr uint32_t lut_lo = 0x03020100u, lut_hi = 0x0C080604u;
+    uint32_t bits = 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool real = (raw[it].valid >> r) & 1u;
-        const uint32_t code = real ? raw[it].code[r] : 0u;
-        const float sh2 = e4m3_half(real ? raw[it].scale[r] : 0u);
-        const uint32_t me = __builtin_amdgcn_perm(lut_hi, lut_lo, code & 0x07070707u);         // even channels
-        const uint32_t mo = __builtin_amdgcn_perm(lut_hi, lut_lo, (code >> 4) & 0x07070707u);  // odd channels
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float f0 = (float)((me >> (8 * j)) & 0xFFu) * sh2;
-          float f1 = (float)((mo >> (8 * j)) & 0xFFu) * sh2;
-          // sign bits of nibbles 2j (bit 8j+3) and 2j+1 (bit 8j+7)
-          f0 = __uint_as_float(__float_as_uint(f0) | ((code << (28 - 8 * j)) & 0x80000000u));
-          f1 = __uint_as_float(__float_as_uint(f1) | ((code << (24 - 8 * j)) & 0x80000000u));
-          d[r][j] = pack_bf16x2(f0, f1);
-        }
-      }
-      store_item<NHG>(sh, rg, cg, d, true, true);
-    } else {
-      uint32_t bits = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int wr = (c - Q.cs) * kChunk + 4 * rg + r;
-        const bool ok = wr < Q.n_w;
-        bits |= (uint32_t)ok << r;
-        const int64_t row = Q.win_row0 + (ok ? wr : 0);
-        const uint4 kv = ok ? *reinterpret_cast<const uint4*>(a.swa_k + row * kAttnC + 8 * cg) : make_uint4(0, 0, 0, 0);
-        d[r][0] = kv.x; d[r][1] = kv.y; d[r][2] = kv.z; d[r][3] = kv.w;
-      }
-      if (cg == 0) sh.vb[rg] = bits;
-      store_item<NHG>(sh, rg, cg, d, true, false);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int wr = (c - Q.cs) * kChunk + 4 * rg + r;
-        const bool ok = wr < Q.n_w;
-        const int64_t row = Q.win_row0 + (ok ? wr : 0);
-        const uint4 vv = ok ? *reinterpret_cast<const uint4*>(a.swa_v + row * kAttnC + 8 * cg) : make_uint4(0, 0, 0, 0);
-        d[r][0] = vv.x; d[r][1] = vv.y; d[r][2] = vv.z; d[r][3] = vv.w;
-      }
-      store_item<NHG>(sh, rg, cg, d, false, true);
+    for (int r = 0; r < 4; ++r) {
+      const int wr = (c - Q.cs) * kChunk + 4 * rg + r;
+      const bool ok = wr < Q.n_w;
+      bits |= (uint32_t)ok << r;
+      const int64_t row = Q.win_row0 + (ok ? wr : 0);
+      raw[it].k[r] = *reinterpret_cast<const uint4*>(a.swa_k + row * kAttnC + 8 * cg);
+      raw[it].v[r] = *reinterpret_cast<const uint4*>(a.swa_v + row * kAttnC + 8 * cg);
     }
+    raw[it].valid = bits;
+  }
+}
+
+// Write one item (4 rows x 8 channels as bf16 pairs d[row][pair]) into a
+// row-major buffer.
+__device__ __forceinline__ void store_rows(uint4* buf, int rg, int cg, const uint32_t (&d)[4][4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) buf[kbuf_unit(4 * rg + r, cg)] = make_uint4(d[r][0], d[r][1], d[r][2], d[r][3]);
+}
+
+template <int NHG>
+__device__ __forceinline__ void commit_sparse(AttnShared<NHG>& sh, const RawSparse (&raw)[kItems / (128 * NHG)]) {
+  constexpr int PER = kItems / (128 * NHG);
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int item = threadIdx.x + it * 128 * NHG;
+    const int rg = item_rows(item), cg = item & 63;
+    const uint32_t valid = raw[it].valid;
+    if (cg == 0) sh.vb[rg] = valid;
+    uint32_t d[4][4];
+    // twice the E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 as bytes
+    constexpr uint32_t lut_lo = 0x03020100u, lut_hi = 0x0C080604u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool real = (valid >> r) & 1u;
+      const uint32_t code = real ? raw[it].code[r] : 0u;
+      const float sh2 = e4m3_half(real ? (raw[it].scale[r] >> (8 * ((cg >> 1) & 3))) & 0xFFu : 0u);
+      const uint32_t me = __builtin_amdgcn_perm(lut_hi, lut_lo, code & 0x07070707u);         // even channels
+      const uint32_t mo = __builtin_amdgcn_perm(lut_hi, lut_lo, (code >> 4) & 0x07070707u);  // odd channels
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float f0 = (float)((me >> (8 * j)) & 0xFFu) * sh2;
+        float f1 = (float)((mo >> (8 * j)) & 0xFFu) * sh2;
+        // sign bits of nibbles 2j (bit 8j+3) and 2j+1 (bit 8j+7)
+        f0 = __uint_as_float(__float_as_uint(f0) | ((code << (28 - 8 * j)) & 0x80000000u));
+        f1 = __uint_as_float(__float_as_uint(f1) | ((code << (24 - 8 * j)) & 0x80000000u));
+        d[r][j] = pack_bf16x2(f0, f1);
+      }
+    }
+    store_rows(sh.kbuf, rg, cg, d);
+  }
+}
+
+template <int NHG>
+__device__ __forceinline__ void commit_window(AttnShared<NHG>& sh, const RawWindow (&raw)[kItems / (128 * NHG)]) {
+  constexpr int PER = kItems / (128 * NHG);
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int item = threadIdx.x + it * 128 * NHG;
+    const int rg = item_rows(item), cg = item & 63;
+    const uint32_t valid = raw[it].valid;
+    if (cg == 0) sh.vb[rg] = valid;
+    uint32_t d[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint4 kv = ((valid >> r) & 1u) ? raw[it].k[r] : make_uint4(0, 0, 0, 0);
+      d[r][0] = kv.x; d[r][1] = kv.y; d[r][2] = kv.z; d[r][3] = kv.w;
+    }
+    store_rows(sh.kbuf, rg, cg, d);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint4 vv = ((valid >> r) & 1u) ? raw[it].v[r] : make_uint4(0, 0, 0, 0);
+      d[r][0] = vv.x; d[r][1] = vv.y; d[r][2] = vv.z; d[r][3] = vv.w;
+    }
+    store_rows(sh.vbuf, rg, cg, d);
   }
 }
 
@@ -238,6 +277,7 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   const int hg = wave >> 1, hc = wave & 1;          // head group, channel half
   const int g = lane / 16, hcol = lane % 16;
   const int head = hg * 16 + hcol;
+  const int idxv = idx_lane_load<NHG>(a, qi, split, lane);
   const QueryInfo Q = query_info(a, qi);
   const int nchunk = Q.cs + Q.cw;
 
@@ -252,14 +292,62 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   for (int t = 0; t < 16; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_use = -__builtin_inff(), l_run = 0.0f;   // P is formed as exp2(x - m_use)
 
-  RawItem raw[PER];
-  int c = split;
-  if (c < nchunk) load_chunk<NHG>(a, Q, qi, c, raw);
-  for (; c < nchunk; c += a.n_split) {
+  // This split's chunks are split + i * n_split: nS sparse ones, then nW window
+  // ones. The first window chunk is loaded with the first sparse chunk and
+  // computed first; the sparse chunks follow, each loaded while the one before
+  // it is computed; further window chunks (only with few splits) are loaded
+  // when they are committed. Only sparse loads are issued inside the loop.
+  const int ns_ = a.n_split;
+  const int nS = split < Q.cs ? (Q.cs - split + ns_ - 1) / ns_ : 0;
+  const int nT = split < nchunk ? (nchunk - split + ns_ - 1) / ns_ : 0;
+  const int nW = nT - nS, w0 = nW > 0 ? 1 : 0;
+  RawSparse rs[PER];
+  RawWindow rw[PER];
+  if (nS > 0) load_sparse<NHG>(a, Q, qi, split, 0, idxv, rs);
+  // (with several items per thread the window slot would not fit in registers
+  // beside the accumulators: the first window chunk is then loaded at commit)
+  if constexpr (PER == 1) {
+    if (nW > 0) load_window<NHG>(a, Q, split + nS * ns_, rw);
+  }
+  // Take delivery of everything loaded so far, once, here (the prologue's
+  // loads were issued together and the first commit needs them anyway): a
+  // register still counted as in flight at the loop head would make every
+  // iteration wait for the loads issued after it (the counter is in order),
+  // which includes the prefetched chunk.
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, qv[kk])));
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    asm volatile("" ::"v"(rs[it].code[0]), "v"(rs[it].code[1]), "v"(rs[it].code[2]), "v"(rs[it].code[3]));
+    asm volatile("" ::"v"(rs[it].scale[0]), "v"(rs[it].scale[1]), "v"(rs[it].scale[2]), "v"(rs[it].scale[3]));
+    if constexpr (PER == 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        asm volatile("" ::"v"(__builtin_bit_cast(u32x4, rw[it].k[r])), "v"(__builtin_bit_cast(u32x4, rw[it].v[r])));
+    }
+  }
+  if constexpr (PER == 1) {
+    if (nW > 0) commit_window<NHG>(sh, rw);   // the loop's first barrier publishes it
+  }
+  for (int step = 0; step < nT; ++step) {
+    const int i = step - w0;              // sparse ordinal when i < nS
+    const bool window = step < w0 || i >= nS;
     __syncthreads();
-    commit_chunk<NHG>(sh, Q, a, c, raw);
+    if (step < w0) {
+      if constexpr (PER != 1) {          // (with one item per thread it was committed before the loop)
+        RawWindow tw[PER];
+        load_window<NHG>(a, Q, split + nS * ns_, tw);
+        commit_window<NHG>(sh, tw);
+      }
+    } else if (i < nS) {
+      commit_sparse<NHG>(sh, rs);
+    } else {
+      RawWindow tw[PER];
+      load_window<NHG>(a, Q, split + (i + 1) * ns_, tw);   // window ordinal i - nS + 1
+      commit_window<NHG>(sh, tw);
+    }
     __syncthreads();
-    if (c + a.n_split < nchunk) load_chunk<NHG>(a, Q, qi, c + a.n_split, raw);
+    if (step >= w0 && i + 1 < nS) load_sparse<NHG>(a, Q, qi, split + (i + 1) * ns_, i + 1, idxv, rs);
 
     // partial S^T over this channel half: A = even rows (tile 0) / odd rows (tile 1), B = Q^T
     v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -319,9 +407,20 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
       phi[i] = h;
       plo[i] = (__bf16)(p[i] - (float)h);
     }
+    uint4* vrows = window ? sh.vbuf : sh.kbuf;    // values: the latent rows themselves, or the window's
+    const int tr_row = 8 * g + (hcol >> 2), tr_half = 8 * (hcol & 1);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const uint4 vtile = sh.vt[vt_unit(256 * hc + 16 * t + hcol, g)];
+      // V^T operand (channels ch0 + hcol, rows 8g .. 8g+7) by two transposing
+      // reads: lane 4a+b of a 16-lane group gets element b of the 8-byte words
+      // addressed by lanes a, 4+a, 8+a, 12+a, so lane i addresses row
+      // 8g + 4h + i/4, channels ch0 + 4(i%4) .. +3.
+      const int u = 32 * hc + 2 * t + ((hcol & 3) >> 1);
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(reinterpret_cast<char*>(vrows + kbuf_unit(tr_row, u)) + tr_half));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(reinterpret_cast<char*>(vrows + kbuf_unit(tr_row + 4, u)) + tr_half));
+      const v8s vtile = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, vtile), phi, o[t], 0, 0, 0);
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, vtile), plo, o[t], 0, 0, 0);
     }
@@ -348,21 +447,30 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge the splits of one (query, head): 128 threads x 4 channels.
+// Merge the splits of one (query, head): 128 threads x 4 channels. Every
+// split's (m, l) and O slice are loaded before any is used, so the S loads of
+// a thread are in flight together.
+template <int S>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int head = blockIdx.x, qi = blockIdx.y;
-  const int S = a.n_split;
-  float M = -__builtin_inff();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[2 * (((int64_t)qi * S + s) * a.Hq + head)]);
-  float L = 0.0f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float2 ml[S];
+  float4 v[S];
+#pragma unroll
   for (int s = 0; s < S; ++s) {
     const int64_t slot = ((int64_t)qi * S + s) * a.Hq + head;
-    const float m = a.part_ml[2 * slot], l = a.part_ml[2 * slot + 1];
-    const float f = (m == -__builtin_inff()) ? 0.0f : exp2f(m - M);
-    L += f * l;
-    const float4 v = reinterpret_cast<const float4*>(a.part_o + slot * kAttnC)[threadIdx.x];
-    acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
+    ml[s] = reinterpret_cast<const float2*>(a.part_ml)[slot];
+    v[s] = reinterpret_cast<const float4*>(a.part_o + slot * kAttnC)[threadIdx.x];
+  }
+  float M = ml[0].x;
+#pragma unroll
+  for (int s = 1; s < S; ++s) M = fmaxf(M, ml[s].x);
+  float L = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const float f = (ml[s].x == -__builtin_inff()) ? 0.0f : exp2f(ml[s].x - M);
+    L += f * ml[s].y;
+    acc.x += f * v[s].x; acc.y += f * v[s].y; acc.z += f * v[s].z; acc.w += f * v[s].w;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   reinterpret_cast<float4*>(a.out + ((int64_t)qi * a.Hq + head) * kAttnC)[threadIdx.x] =
@@ -404,7 +512,14 @@ hipError_t launch_attn(AttnArgs a, void* ws, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  attn_combine_kernel<<<dim3((uint32_t)a.Hq, (uint32_t)a.nq), dim3(128), 0, stream>>>(a);
+  const dim3 cgrid((uint32_t)a.Hq, (uint32_t)a.nq);
+  switch (a.n_split) {
+    case 2: attn_combine_kernel<2><<<cgrid, dim3(128), 0, stream>>>(a); break;
+    case 4: attn_combine_kernel<4><<<cgrid, dim3(128), 0, stream>>>(a); break;
+    case 8: attn_combine_kernel<8><<<cgrid, dim3(128), 0, stream>>>(a); break;
+    case 16: attn_combine_kernel<16><<<cgrid, dim3(128), 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

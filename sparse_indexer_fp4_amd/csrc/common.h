@@ -10,6 +10,9 @@ constexpr int kWave = 64;
 // Operand and result types of v_mfma_f32_16x16x32_bf16.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
 
 // max(x, 0) for finite x as one v_med3 (fmaxf would add a NaN-quieting step).
 __device__ __forceinline__ float relu_f(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f); }

@@ -362,6 +362,19 @@ def test_abi_rejects_bad_arguments(fk, gpu):
     with pytest.raises(fk.Fp4kvError) as e:
         fk.fp4kv_index_full(q3, w[:, :3].contiguous(), kk, ss, qp, 1, 64, 8, 8)
     assert e.value.status == -4
+    # attention reads the scales as aligned 32-bit words: a scales pointer off
+    # a 4-byte boundary is refused before anything is launched
+    qa = torch.zeros((1, 16, 512), dtype=torch.bfloat16, device=gpu)
+    sbuf = torch.zeros(4 * 32 + 4, dtype=torch.uint8, device=gpu)
+    idx = torch.zeros((1, 8), dtype=torch.int32, device=gpu)
+    nidx = torch.ones(1, dtype=torch.int32, device=gpu)
+    win = torch.zeros((1, 8, 512), dtype=torch.bfloat16, device=gpu)
+    with pytest.raises(fk.Fp4kvError) as e:
+        fk.fp4kv_sparse_attn_decode(qa, codes, sbuf[1:1 + 4 * 32].view(4, 32), ss, idx, nidx, win, win, qp, 1.0)
+    assert e.value.status == -2
+    out, _ = fk.fp4kv_sparse_attn_decode(qa, codes, sbuf[4:4 + 4 * 32].view(4, 32), ss, idx, nidx, win, win, qp, 1.0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
 
 
 def test_repeatable_bits(fk, gpu):
