@@ -143,20 +143,25 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
     }
   }
 
-  // Store the workgroup's results: scores (and block maxima) of nsteps*64 slots.
-  for (int step = 0; step < nsteps; ++step) {
-    const int64_t j = first + (int64_t)step * 64 + lane;
-    const float score = res[step * 64 + lane];
-    const int64_t t = position(j);
-    if (REINDEX) {
-      if (j < (int64_t)a.P * 8) a.pool_scores[(int64_t)qi * a.P * 8 + j] = t >= 0 ? score : 0.0f;
-    } else {
-      if (t >= 0) a.scores[(int64_t)qi * a.max_ctx + t] = score;
-      float bm = t >= 0 ? score : -__builtin_inff();
-      bm = fmaxf(bm, __shfl_xor(bm, 1));
-      bm = fmaxf(bm, __shfl_xor(bm, 2));
-      bm = fmaxf(bm, __shfl_xor(bm, 4));
-      if ((lane & 7) == 0 && t >= 0) a.blockmax[(int64_t)qi * a.nblk_max + (t >> 3)] = bm;
+  // Store the workgroup's results: scores (and block maxima) of nsteps*64
+  // slots. All scores are read from LDS first (one wait), the block maxima come
+  // from DPP exchanges inside each group of 8 lanes, and the stores are issued
+  // back to back, so the workgroup leaves its slot soon after its last load.
+  float sv[MAXSTEPS];
+#pragma unroll
+  for (int step = 0; step < MAXSTEPS; ++step) sv[step] = step < nsteps ? res[step * 64 + lane] : 0.0f;
+#pragma unroll
+  for (int step = 0; step < MAXSTEPS; ++step) {
+    if (step < nsteps) {
+      const int64_t j = first + (int64_t)step * 64 + lane;
+      const int64_t t = position(j);
+      if (REINDEX) {
+        if (j < (int64_t)a.P * 8) a.pool_scores[(int64_t)qi * a.P * 8 + j] = t >= 0 ? sv[step] : 0.0f;
+      } else {
+        if (t >= 0) a.scores[(int64_t)qi * a.max_ctx + t] = sv[step];
+        const float bm = max8(t >= 0 ? sv[step] : -__builtin_inff());
+        if ((lane & 7) == 0 && t >= 0) a.blockmax[(int64_t)qi * a.nblk_max + (t >> 3)] = bm;
+      }
     }
   }
 }

@@ -50,16 +50,6 @@ __device__ __forceinline__ int64_t mq_visible(const ScanArgs& a, int q, int64_t 
   return n < 0 ? 0 : n;
 }
 
-// Maximum over each aligned group of 8 lanes, left in every lane of the group
-// (DPP: swap neighbours, swap pairs, then mirror the halves of each 8 lanes).
-__device__ __forceinline__ float max8(float v) {
-  int x = __float_as_int(v);
-  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false)), 3.402823466e38f));
-  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false)), 3.402823466e38f));
-  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false)), 3.402823466e38f));
-  return __int_as_float(x);
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
