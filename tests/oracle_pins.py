@@ -20,7 +20,7 @@ import numpy as np
 import scipy.special
 import torch
 
-from oracle import attention, chain, fp4, indexer
+from oracle import attention, chain, fp4, indexer, kvformats
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -143,6 +143,151 @@ def check_byte_accounting():
     assert abs(2 * C / b - c["bf16_over_fp4_approx"]) < 0.5       # 3.56
     assert c["pool_blocks"] * c["block_tokens"] == c["pool_positions"] == c["pool_positions_approx"]
     assert indexer.BLOCK == c["block_tokens"]
+
+
+# --------------------------------------------------- KV format variants ----
+
+def all_bf16_finite():
+    """Every finite bfloat16 value of either sign, as float64."""
+    pos = np.arange(0x7F80, dtype=np.uint32)
+    bits = np.concatenate([pos, pos | 0x8000]) << 16
+    return bits.view(np.float32).astype(np.float64)
+
+
+def check_fp8_encode_exhaustive():
+    """E4M3FN codes of every finite bf16 value equal torch's round-to-nearest-even
+    float8_e4m3fn cast wherever that cast is finite (|x| <= 464); beyond it the
+    oracle saturates at 448 (torch returns NaN there)."""
+    x = all_bf16_finite()
+    got = kvformats.fp8_encode(x)
+    inr = np.abs(x) <= 464.0
+    ref = torch.from_numpy(x[inr].astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    bad = np.nonzero(got[inr] != ref)[0]
+    assert bad.size == 0, (bad.size, x[inr][bad[:5]], got[inr][bad[:5]], ref[bad[:5]])
+    out = ~inr
+    assert (got[out] & 0x7F == 0x7E).all() and np.array_equal(got[out] >> 7, np.signbit(x[out]).astype(np.uint8))
+    # decode of the encoding is the value itself wherever x is an E4M3 value
+    vals = fp4.E4M3_TABLE[:127]
+    assert np.array_equal(kvformats.fp8_dequantize_rows(kvformats.fp8_encode(vals)), vals)
+    assert np.array_equal(kvformats.fp8_dequantize_rows(kvformats.fp8_encode(-vals)), -vals)
+
+
+def check_fp8_worked_values():
+    """Hand-worked E4M3FN codes: 1 -> 0x38; 448 and 500 -> 0x7E (saturation);
+    -0 -> 0x80; 2^-9 -> 0x01 (smallest subnormal); 2^-10 -> 0x00 and
+    3 * 2^-10 -> 0x02 (ties to the even code); 17 -> 0x58 (16, the even neighbour
+    of the tie 16 | 18)."""
+    x = np.array([1.0, 448.0, 500.0, -0.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10, 17.0])
+    assert kvformats.fp8_encode(x).tolist() == [0x38, 0x7E, 0x7E, 0x80, 0x01, 0x00, 0x02, 0x58]
+
+
+def _bf16_floor_log2(bits):
+    """floor(log2 v) of a positive finite bf16 value from its bit fields."""
+    e = (bits >> 7) & 0xFF
+    m = bits & 0x7F
+    if e > 0:
+        return int(e) - 127
+    return -133 + int(m).bit_length() - 1          # subnormal: v = m * 2^-133
+
+
+def check_mx_shared_exponent_exhaustive():
+    """The MX shared exponent of every positive finite bf16 amax equals
+    floor(log2 amax) - 2 read off the bf16 exponent field (subnormals from the
+    leading mantissa bit), clamped to [-127, 127]; 0 gives -127."""
+    bits = np.arange(1, 0x7F80, dtype=np.uint32)
+    a = (bits << 16).view(np.float32).astype(np.float64)
+    got = kvformats.mx_shared_exponent(a)
+    ref = np.array([min(max(_bf16_floor_log2(int(b)) - 2, -127), 127) for b in bits])
+    assert np.array_equal(got, ref), np.nonzero(got != ref)[0][:5]
+    assert kvformats.mx_shared_exponent(np.array([0.0]))[0] == -127
+    assert kvformats.E8M0_TABLE[0] == 2.0 ** -127 and kvformats.E8M0_TABLE[254] == 2.0 ** 127
+    assert math.isnan(kvformats.E8M0_TABLE[255])
+
+
+def _mxfp4_bruteforce(block):
+    """MXFP4 of one 32-value block with exact rationals: X = 2^(floor(log2 amax) - 2),
+    then per value the nearest of {0, .5, 1, 1.5, 2, 3, 4, 6} to |x| / X (ties to
+    the even code), sign bit from x."""
+    from fractions import Fraction
+    fr = [Fraction(float(v)) for v in block]
+    amax = max(abs(v) for v in fr)
+    if amax == 0:
+        e = -127
+    else:
+        e = amax.numerator.bit_length() - amax.denominator.bit_length()
+        if Fraction(2) ** e > amax:
+            e -= 1                                     # floor(log2 amax)
+        e = min(max(e - 2, -127), 127)
+    X = Fraction(2) ** e
+    grid = [Fraction(v) for v in (0, 0.5, 1, 1.5, 2, 3, 4, 6)]
+    codes = []
+    for v, f in zip(block, fr):
+        r = abs(f) / X
+        d = [abs(r - g) for g in grid]
+        best = min(d)
+        cand = [i for i, di in enumerate(d) if di == best]
+        mag = cand[0] if len(cand) == 1 else [i for i in cand if i % 2 == 0][0]
+        codes.append((8 if math.copysign(1.0, float(v)) < 0 else 0) | mag)
+    return codes, e + 127
+
+
+def check_mxfp4_bruteforce():
+    """MXFP4 rows (normal data with outliers, exact grid points and midpoints,
+    values saturating in [6, 8) * 2^e, subnormal and all-zero blocks) equal the
+    exact-rational brute force block by block."""
+    rng = np.random.default_rng(7)
+    rows = []
+    for kind in range(6):
+        for _ in range(4):
+            if kind == 0:
+                r = rng.standard_normal(64) * np.where(rng.random(64) < 0.05, 20.0, 1.0)
+            elif kind == 1:                      # grid points and midpoints times one power of two
+                e = int(rng.integers(-20, 20))
+                r = rng.choice([0, .25, .5, .75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6], 64) * 2.0 ** e
+                r[0] = 6 * 2.0 ** e
+                r *= rng.choice([-1.0, 1.0], 64)
+            elif kind == 2:                      # saturation: amax in [6, 8) * 2^e
+                r = rng.uniform(-8, 8, 64) * 2.0 ** int(rng.integers(-5, 5))
+            elif kind == 3:                      # bf16 subnormals and tiny values
+                r = rng.standard_normal(64) * 2.0 ** -130
+            elif kind == 4:
+                r = np.zeros(64)
+                r[rng.integers(0, 64)] = -0.0
+            else:                                # huge values near the bf16 maximum
+                r = rng.standard_normal(64) * 2.0 ** 120
+            rows.append(r)
+    x = torch.tensor(np.array(rows), dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    codes, scales = kvformats.mxfp4_quantize_rows(x)
+    for i in range(x.shape[0]):
+        for g in range(2):
+            bc, bs = _mxfp4_bruteforce(x[i, 32 * g:32 * g + 32])
+            got = []
+            for j in range(16):
+                byte = int(codes[i, 16 * g + j])
+                got += [byte & 0xF, byte >> 4]
+            assert got == bc and int(scales[i, g]) == bs, (i, g)
+
+
+def check_mxfp4_roundtrip():
+    """Blocks of exact MXFP4 values (E2M1 values times 2^e, with one of magnitude
+    4 * 2^e or 6 * 2^e fixing the shared exponent at e) decode to themselves."""
+    rng = np.random.default_rng(11)
+    for e in (-127, -60, -3, 0, 5, 60, 125):
+        v = rng.choice(fp4.E2M1_TABLE[:16], (3, 32)) * 2.0 ** e
+        v[:, 0] = rng.choice([4.0, 6.0, -4.0, -6.0], 3) * 2.0 ** e
+        codes, scales = kvformats.mxfp4_quantize_rows(v)
+        assert (scales == e + 127).all(), e
+        assert np.array_equal(kvformats.mxfp4_dequantize_rows(codes, scales), v), e
+
+
+def check_kv_format_bytes():
+    """Bytes per 512-channel row: FP4 with E4M3 per 16 = 288, MXFP4 = 256 + 16 =
+    272, FP8 = 512. FP4 is 0.5625 of FP8, the pages' "roughly half"."""
+    c = pages_constants()
+    C = 512
+    b = [kvformats.bytes_per_row(f, C) for f in (kvformats.FMT_FP4, kvformats.FMT_MXFP4, kvformats.FMT_FP8)]
+    assert b == [288, 272, 512] and b[0] == fp4.bytes_per_row(C)
+    assert abs(b[0] / b[2] - c["fp4_over_fp8_approx"]) < 0.1
 
 
 # -------------------------------------------------------------- indexer ----

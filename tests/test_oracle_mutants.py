@@ -6,7 +6,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import attention, chain, fp4, indexer
+from oracle import attention, chain, fp4, indexer, kvformats
 from tests import oracle_pins
 
 
@@ -110,6 +110,43 @@ def _layers_reuse_full(modes, full_fn, reindex_fn):
     return out
 
 
+def _mx_exponent_minus_one(amax):
+    a = np.asarray(amax, float)
+    _, e = np.frexp(a)
+    return np.where(a == 0, -127, np.clip(e.astype(np.int64) - 1 - 1, -127, 127))
+
+
+def _mx_exponent_ceil(amax):
+    a = np.asarray(amax, float)
+    _, e = np.frexp(a)
+    exact = np.ldexp(0.5, e) == a
+    fl = e.astype(np.int64) - 1
+    return np.where(a == 0, -127, np.clip(np.where(exact, fl, fl + 1) - 2, -127, 127))
+
+
+def _mx_scale_bias_128(x):
+    codes, scales = kvformats.__dict__["_orig_mxfp4_quantize_rows"](x)
+    return codes, (scales.astype(np.int64) + 1).astype(np.uint8)
+
+
+def _fp8_ties_up(x):
+    x = np.asarray(x, float)
+    pos = fp4.E4M3_TABLE[:127]
+    ax = np.minimum(np.abs(x), 448.0)
+    d = np.abs(ax[..., None] - pos)
+    mag = 126 - np.argmin(d[..., ::-1], axis=-1)
+    return ((np.signbit(x).astype(int) << 7) | mag).astype(np.uint8)
+
+
+def _fp8_sign_dropped(x):
+    return kvformats.__dict__["_orig_fp8_encode"](np.abs(np.asarray(x, float)))
+
+
+def _fp8_overflow_nan(x):
+    c = kvformats.__dict__["_orig_fp8_encode"](x)
+    return np.where(np.abs(np.asarray(x, float)) > 448.0, c | 0x7F, c).astype(np.uint8)
+
+
 MUTANTS = [
     ("scores: no ReLU", indexer, "token_scores", _no_relu),
     ("scores: dropped head", indexer, "token_scores", _drop_last_head),
@@ -129,6 +166,12 @@ MUTANTS = [
     ("reindex ignores the pool", indexer, "index_reindex", _reindex_everything),
     ("full sees position q_pos+1", indexer, "index_full", _full_sees_next),
     ("reuse copies the Full layer", chain, "layer_indices", _layers_reuse_full),
+    ("MX exponent floor(log2) - 1", kvformats, "mx_shared_exponent", _mx_exponent_minus_one),
+    ("MX exponent from ceil(log2)", kvformats, "mx_shared_exponent", _mx_exponent_ceil),
+    ("MX scale byte biased by 128", kvformats, "mxfp4_quantize_rows", _mx_scale_bias_128),
+    ("FP8 ties upward", kvformats, "fp8_encode", _fp8_ties_up),
+    ("FP8 sign dropped", kvformats, "fp8_encode", _fp8_sign_dropped),
+    ("FP8 overflow to NaN", kvformats, "fp8_encode", _fp8_overflow_nan),
 ]
 
 
