@@ -14,6 +14,10 @@ One step = the whole hot path of the layer for the batch:
   fp4kv_index_select      (top-2,048 blocks -> pool -> top-512 tokens)
   fp4kv_sparse_attn_decode (FP4 gather-dequant attention + window + LSE merge)
 
+--kv-format mxfp4|fp8 runs the same step over a main-KV cache in one of the
+formats the pages compare FP4 with (E2M1 + E8M0 per 32 channels; E4M3 per
+channel), appended and attended through the format-generic entry points.
+
 Prints one JSON line: the metric (queries/s), the step time, the roofline of
 the dominant kernel (the scan: algorithmic bytes per launch over its measured
 launch time, against 8 TB/s, with the HBM traffic the byte counters measured)
@@ -45,7 +49,11 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(cfg):
+KV_FORMATS = {"fp4": 0, "mxfp4": 1, "fp8": 2}
+KV_ROW_BYTES = {"fp4": 512 // 2 + 512 // 16, "mxfp4": 512 // 2 + 512 // 32, "fp8": 512}   # at C = 512
+
+
+def algorithmic_bytes(cfg, kv_format="fp4"):
     """Compulsory HBM bytes per call, counting inputs once and outputs once."""
     B, N = cfg.n_seq, cfg.ctx
     nblk = (N + 7) // 8
@@ -56,8 +64,8 @@ def algorithmic_bytes(cfg):
     select = (B * nblk * 4                       # block maxima read
               + B * cfg.P * 8 * 4                # pool token scores read
               + B * (cfg.P + cfg.k + 2) * 4)     # pool, indices, counts written
-    row = cfg.C // 2 + cfg.C // 16               # 288 B per FP4 row
-    attn = B * (cfg.k * row                      # gathered FP4 rows
+    row = KV_ROW_BYTES[kv_format]                # 288 B per FP4 row
+    attn = B * (cfg.k * row                      # gathered main-KV rows
                 + cfg.k * 4                      # indices
                 + cfg.Hq * cfg.C * 2             # main Q
                 + 2 * cfg.W * cfg.C * 2          # window K and V
@@ -78,7 +86,7 @@ def scan_traffic():
     return SCAN_TRAFFIC["bytes_per_launch"] if h.hexdigest()[:16] == SCAN_TRAFFIC["sources_sha256_16"] else None
 
 
-def cpu_baseline(cfg, n_sample, min_seconds=10.0):
+def cpu_baseline(cfg, n_sample, min_seconds=10.0, kv_format="fp4"):
     """The oracle, as it stands, on n_sample queries of the same workload:
     Full-layer indexer + attention per query, passes over the sample repeated until
     min_seconds of CPU work. Input generation is not timed."""
@@ -87,7 +95,7 @@ def cpu_baseline(cfg, n_sample, min_seconds=10.0):
     from synth import bf16_to_f64
     from synth import workloads as wl
     from tests import oracle_runner as orun
-    from oracle import attention, fp4, indexer
+    from oracle import attention, indexer, kvformats
 
     torch.set_num_threads(os.cpu_count() or 1)
     prepared = []
@@ -113,7 +121,8 @@ def cpu_baseline(cfg, n_sample, min_seconds=10.0):
             tg = time.perf_counter()
             x = bf16_to_f64(wl.kv_rows(cfg, s, torch.from_numpy(idx)))
             t_gen += time.perf_counter() - tg
-            rows = fp4.dequantize_rows(*fp4.quantize_rows(x))
+            fmt = KV_FORMATS[kv_format]
+            rows = kvformats.dequantize_rows(fmt, *kvformats.quantize_rows(fmt, x))
             attention.attend(Q, rows, wk, wv, cfg.scale)
             done += 1
     dt = time.perf_counter() - t0 - t_gen
@@ -136,6 +145,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-sample", type=int, default=32, help="queries timed on the oracle (0: skip)")
+    ap.add_argument("--kv-format", choices=sorted(KV_FORMATS), default="fp4",
+                    help="main-KV cache format (default fp4: E2M1 + E4M3 per 16 channels)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes, --steps times (calibrates "
                          "the HBM byte counters against a kernel of known traffic), then exit")
@@ -165,7 +176,18 @@ def main():
     cfg = wl.CONFIGS["decode128k"]
     t0 = time.perf_counter()
     log(f"generating {cfg.name} inputs on the GPU")
-    dw = DeviceWorkload(cfg, dev)
+    fmt = KV_FORMATS[args.kv_format]
+    dw = DeviceWorkload(cfg, dev, build_kv=(fmt == 0))
+    codes, scales = dw.codes, dw.scales
+    if fmt != 0:
+        codes = torch.zeros((dw.total_rows, fk.fp4kv_kv_code_bytes(fmt, cfg.C)), dtype=torch.uint8, device=dev)
+        sb = fk.fp4kv_kv_scale_bytes(fmt, cfg.C)
+        scales = torch.zeros((dw.total_rows, sb), dtype=torch.uint8, device=dev) if sb > 0 else None
+        starts = cfg.seq_starts()
+        for sq in range(cfg.n_seq):
+            for a, b in wl.chunks(int(dw.lengths[sq]), 1 << 18):
+                fk.fp4kv_kv_append(fmt, wl.kv_rows_into(cfg, sq, a, b, dev), codes, scales,
+                                   dst_start=int(starts[sq]) + a)
     new_x, new_dst = dw.newest_rows()
     B, N = cfg.n_seq, cfg.ctx
     nblk = (N + 7) // 8
@@ -191,7 +213,10 @@ def main():
         more than two event records."""
         if ev is not None:
             ev[0].record(stream)
-        fk.fp4kv_quantize_append(new_x, dw.codes, dw.scales, dst_rows=new_dst, stream=stream)
+        if fmt == 0:
+            fk.fp4kv_quantize_append(new_x, codes, scales, dst_rows=new_dst, stream=stream)
+        else:
+            fk.fp4kv_kv_append(fmt, new_x, codes, scales, dst_rows=new_dst, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         if scan_ev is not None:
@@ -206,8 +231,14 @@ def main():
                               pool_out=pool, n_pool=n_pool, idx_out=idx, n_idx=n_idx, stream=stream)
         if ev is not None:
             ev[3].record(stream)
-        fk.fp4kv_sparse_attn_decode(dw.q[0], dw.codes, dw.scales, dw.seq_start, idx, n_idx, dw.swa_k[0],
-                                    dw.swa_v[0], dw.q_pos, cfg.scale, out=out, lse=lse, workspace=aws, stream=stream)
+        if fmt == 0:
+            fk.fp4kv_sparse_attn_decode(dw.q[0], codes, scales, dw.seq_start, idx, n_idx, dw.swa_k[0],
+                                        dw.swa_v[0], dw.q_pos, cfg.scale, out=out, lse=lse, workspace=aws,
+                                        stream=stream)
+        else:
+            fk.fp4kv_sparse_attn_decode_kv(fmt, dw.q[0], codes, scales, dw.seq_start, idx, n_idx, dw.swa_k[0],
+                                           dw.swa_v[0], dw.q_pos, cfg.scale, out=out, lse=lse, workspace=aws,
+                                           stream=stream)
         if ev is not None:
             ev[4].record(stream)
 
@@ -238,7 +269,7 @@ def main():
     per = {k: v / n_bd for k, v in per.items()}          # ms per launch, breakdown pass
     per["scan_timed_region"] = scan_ms
     ms_step = 1e3 * elapsed / args.steps
-    nbytes = algorithmic_bytes(cfg)
+    nbytes = algorithmic_bytes(cfg, args.kv_format)
     scan_gbps = nbytes["scan"] / (scan_ms * 1e-3) / 1e9
     layer_gbps = nbytes["layer"] / (ms_step * 1e-3) / 1e9
 
@@ -256,9 +287,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "decode128k: Full-layer decode step, 32 queries x 131,072-token contexts, "
-                               "indexer 16x128, pool 2,048 blocks of 8, top-512, 64 heads x 512-channel FP4 latent, "
-                               "128-token bf16 window",
+                               "indexer 16x128, pool 2,048 blocks of 8, top-512, 64 heads x 512-channel "
+                               + {"fp4": "FP4 (E2M1 + E4M3 per 16)", "mxfp4": "MXFP4 (E2M1 + E8M0 per 32)",
+                                  "fp8": "FP8 (E4M3 per channel)"}[args.kv_format]
+                               + " latent, 128-token bf16 window",
                    "batch": B, "ctx": N, "pool_blocks": cfg.P, "top_k": cfg.k, "heads": cfg.Hq,
+                   "kv_format": args.kv_format, "kv_bytes_per_row": KV_ROW_BYTES[args.kv_format],
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "indexer scan (fp4kv_index_scores)",
                      "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -268,7 +302,7 @@ def main():
     }
     if args.cpu_sample > 0:
         log(f"timing the oracle on {args.cpu_sample} queries")
-        rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
+        rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample, kv_format=args.kv_format)
     else:
         rec["cpu_baseline"] = None
     log(f"done in {time.perf_counter() - t0:.1f} s")

@@ -101,6 +101,47 @@ fp4kv_status fp4kv_quantize_append(const void* src, int64_t n_rows, int32_t C,
                                    void* stream);
 
 /*
+ * Main-KV storage formats. The FP4 cache above is format 0. Formats 1 and 2 are
+ * the formats the pages compare it with, for measuring the storage, bandwidth
+ * and accuracy trade: [T] "Mechanism 3" names the KV format MXFP4, and [G] FP4
+ * main KV paragraph and [N] "FP4 KV Quantization and Cache Lifetime Management"
+ * say FP4 takes about half the bytes of an FP8 cache.
+ *   FP4KV_KV_FP4    E2M1 codes + one E4M3 scale per 16 channels (as above);
+ *                   C/2 + C/16 bytes per row (288 at C = 512).
+ *   FP4KV_KV_MXFP4  E2M1 codes + one E8M0 scale per 32 channels (OCP
+ *                   microscaling): per block, e = floor(log2 amax) - 2 clamped
+ *                   to [-127, 127] (-127 if amax = 0), scale byte e + 127, each
+ *                   value the E2M1 code nearest x / 2^e (ties to the even code,
+ *                   saturating at 6). Codes as for FP4; scales uint8
+ *                   [rows, C/32]; 272 bytes per row at C = 512.
+ *   FP4KV_KV_FP8    one E4M3FN code per channel (nearest finite value, ties to
+ *                   the even code, saturating at 448, sign bit of x); codes
+ *                   uint8 [rows, C], no scale plane; 512 bytes per row.
+ */
+enum {
+    FP4KV_KV_FP4 = 0,
+    FP4KV_KV_MXFP4 = 1,
+    FP4KV_KV_FP8 = 2
+};
+
+/* Bytes per row of the code plane and of the scale plane of format fmt (-1 for
+ * an unknown format or a C that is not a positive multiple of 32). */
+int64_t fp4kv_kv_code_bytes(int32_t fmt, int32_t C);
+int64_t fp4kv_kv_scale_bytes(int32_t fmt, int32_t C);
+
+/*
+ * Quantize-append of main-KV rows in format fmt; arguments as for
+ * fp4kv_quantize_append (which is this call with FP4KV_KV_FP4), with codes
+ * [cap_rows, fp4kv_kv_code_bytes(fmt, C)] and scales
+ * [cap_rows, fp4kv_kv_scale_bytes(fmt, C)]. scales may be NULL for
+ * FP4KV_KV_FP8. Codes are exact, as for FP4.
+ * Errors: as for fp4kv_quantize_append; an unknown fmt (FP4KV_ERR_UNSUPPORTED).
+ */
+fp4kv_status fp4kv_kv_append(int32_t fmt, const void* src, int64_t n_rows, int32_t C,
+                             const int64_t* dst_rows, int64_t dst_start, uint8_t* codes,
+                             uint8_t* scales, int64_t cap_rows, void* stream);
+
+/*
  * Workspace bytes fp4kv_index_full needs for n_q queries whose positions are
  * below max_ctx (token scores and block maxima, fp32).
  */
@@ -273,6 +314,34 @@ fp4kv_status fp4kv_sparse_attn_prefill(const void* q, const uint8_t* codes,
                                        int32_t Hq, int32_t C, int32_t k, int32_t W,
                                        float scale, float* out, float* lse, void* workspace,
                                        size_t ws_bytes, void* stream);
+
+/*
+ * The two attention calls for a cache in format fmt (see FP4KV_KV_*); every
+ * other argument as for fp4kv_sparse_attn_decode / fp4kv_sparse_attn_prefill,
+ * which are these calls with FP4KV_KV_FP4. codes and scales are laid out as
+ * fp4kv_kv_append writes them; scales is not read (and may be NULL) for
+ * FP4KV_KV_FP8. Rows are dequantised exactly to bf16 for every format. The
+ * append writes MXFP4 scale bytes up to 252 only; bytes 253 and 254 decode
+ * to values beyond bf16, and 255 (NaN) and the FP8 NaN codes 0x7F and 0xFF
+ * are not supported.
+ * Errors: as for the FP4 calls; an unknown fmt (FP4KV_ERR_UNSUPPORTED).
+ */
+fp4kv_status fp4kv_sparse_attn_decode_kv(int32_t fmt, const void* q, const uint8_t* codes,
+                                         const uint8_t* scales, int64_t total_rows,
+                                         const int64_t* seq_start, const int32_t* idx,
+                                         const int32_t* n_idx, const void* swa_k,
+                                         const void* swa_v, const int32_t* q_pos, int32_t B,
+                                         int32_t Hq, int32_t C, int32_t k, int32_t W,
+                                         float scale, float* out, float* lse, void* workspace,
+                                         size_t ws_bytes, void* stream);
+fp4kv_status fp4kv_sparse_attn_prefill_kv(int32_t fmt, const void* q, const uint8_t* codes,
+                                          const uint8_t* scales, int64_t total_rows,
+                                          int64_t seq_start, const int32_t* idx,
+                                          const int32_t* n_idx, const void* swa_k,
+                                          const void* swa_v, int32_t pos0, int32_t T,
+                                          int32_t Hq, int32_t C, int32_t k, int32_t W,
+                                          float scale, float* out, float* lse, void* workspace,
+                                          size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

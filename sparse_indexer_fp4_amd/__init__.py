@@ -45,7 +45,17 @@ _SIGS = {
                                         _f32, _p, _p, _p, _sz, _p]),
     "fp4kv_sparse_attn_prefill": (_i32, [_p, _p, _p, _i64, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                          _i32, _f32, _p, _p, _p, _sz, _p]),
+    "fp4kv_kv_code_bytes": (_i64, [_i32, _i32]),
+    "fp4kv_kv_scale_bytes": (_i64, [_i32, _i32]),
+    "fp4kv_kv_append": (_i32, [_i32, _p, _i64, _i32, _p, _i64, _p, _p, _i64, _p]),
+    "fp4kv_sparse_attn_decode_kv": (_i32, [_i32, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                           _i32, _f32, _p, _p, _p, _sz, _p]),
+    "fp4kv_sparse_attn_prefill_kv": (_i32, [_i32, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                            _i32, _i32, _f32, _p, _p, _p, _sz, _p]),
 }
+
+# Main-KV formats (FP4KV_KV_* in the header).
+KV_FP4, KV_MXFP4, KV_FP8 = 0, 1, 2
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
     _fn.restype = _res
@@ -220,4 +230,63 @@ def fp4kv_sparse_attn_prefill(q, codes, scales, seq_start, idx, n_idx, swa_k, sw
     _check(lib.fp4kv_sparse_attn_prefill(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[0], int(seq_start),
                                          _ptr(idx), _ptr(n_idx), _ptr(swa_k), _ptr(swa_v), int(pos0), T, Hq, C, k, W,
                                          float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, lse
+
+
+def fp4kv_kv_code_bytes(fmt, C):
+    return lib.fp4kv_kv_code_bytes(fmt, C)
+
+
+def fp4kv_kv_scale_bytes(fmt, C):
+    return lib.fp4kv_kv_scale_bytes(fmt, C)
+
+
+def fp4kv_kv_append(fmt, src, codes, scales, dst_rows=None, dst_start=0, stream=None):
+    """Quantize-append of bf16 rows src [n, C] in format fmt into codes [cap, code bytes]
+    and scales [cap, scale bytes] (scales may be None for KV_FP8)."""
+    _expect(src, torch.bfloat16, "src"); _expect(codes, torch.uint8, "codes")
+    if scales is not None:
+        _expect(scales, torch.uint8, "scales")
+    if dst_rows is not None:
+        _expect(dst_rows, torch.int64, "dst_rows")
+    n, C = src.shape
+    _check(lib.fp4kv_kv_append(fmt, _ptr(src), n, C, _ptr(dst_rows), dst_start, _ptr(codes), _ptr(scales),
+                               codes.shape[0], _stream(stream)))
+
+
+def fp4kv_sparse_attn_decode_kv(fmt, q, codes, scales, seq_start, idx, n_idx, swa_k, swa_v, q_pos, scale,
+                                out=None, lse=None, workspace=None, stream=None):
+    """Decode attention over a cache in format fmt (scales may be None for KV_FP8)."""
+    _expect(q, torch.bfloat16, "q"); _expect(swa_k, torch.bfloat16, "swa_k"); _expect(swa_v, torch.bfloat16, "swa_v")
+    _expect(idx, torch.int32, "idx"); _expect(n_idx, torch.int32, "n_idx")
+    B, Hq, C = q.shape
+    k = idx.shape[1]
+    W = swa_k.shape[1]
+    dev = q.device
+    out = torch.empty((B, Hq, C), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    ws = _workspace(fp4kv_attn_workspace_bytes(B, Hq, C, k, W), dev, workspace)
+    _check(lib.fp4kv_sparse_attn_decode_kv(fmt, _ptr(q), _ptr(codes), _ptr(scales), codes.shape[0], _ptr(seq_start),
+                                           _ptr(idx), _ptr(n_idx), _ptr(swa_k), _ptr(swa_v), _ptr(q_pos), B, Hq, C, k,
+                                           W, float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                           _stream(stream)))
+    return out, lse
+
+
+def fp4kv_sparse_attn_prefill_kv(fmt, q, codes, scales, seq_start, idx, n_idx, swa_k, swa_v, pos0, W, scale,
+                                 out=None, lse=None, workspace=None, stream=None):
+    """Prefill-chunk attention over a cache in format fmt (scales may be None for KV_FP8)."""
+    _expect(q, torch.bfloat16, "q"); _expect(swa_k, torch.bfloat16, "swa_k"); _expect(swa_v, torch.bfloat16, "swa_v")
+    T, Hq, C = q.shape
+    k = idx.shape[1]
+    if swa_k.shape[0] != T + W - 1 or swa_v.shape[0] != T + W - 1:
+        raise ValueError("swa_k/swa_v must hold T+W-1 rows")
+    dev = q.device
+    out = torch.empty((T, Hq, C), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((T, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    ws = _workspace(fp4kv_attn_workspace_bytes(T, Hq, C, k, W), dev, workspace)
+    _check(lib.fp4kv_sparse_attn_prefill_kv(fmt, _ptr(q), _ptr(codes), _ptr(scales), codes.shape[0], int(seq_start),
+                                            _ptr(idx), _ptr(n_idx), _ptr(swa_k), _ptr(swa_v), int(pos0), T, Hq, C, k,
+                                            W, float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                            _stream(stream)))
     return out, lse

@@ -50,21 +50,40 @@ int32_t fp4kv_abi_version(void) { return FP4KV_ABI_VERSION; }
 
 const char* fp4kv_last_error(void) { return g_error.c_str(); }
 
+static bool valid_fmt(int32_t fmt) { return fmt >= FP4KV_KV_FP4 && fmt <= FP4KV_KV_FP8; }
+
+int64_t fp4kv_kv_code_bytes(int32_t fmt, int32_t C) {
+  if (!valid_fmt(fmt) || C <= 0 || C % 32 != 0) return -1;
+  return fmt == FP4KV_KV_FP8 ? C : C / 2;
+}
+
+int64_t fp4kv_kv_scale_bytes(int32_t fmt, int32_t C) {
+  if (!valid_fmt(fmt) || C <= 0 || C % 32 != 0) return -1;
+  return fmt == FP4KV_KV_FP4 ? C / 16 : (fmt == FP4KV_KV_MXFP4 ? C / 32 : 0);
+}
+
+fp4kv_status fp4kv_kv_append(int32_t fmt, const void* src, int64_t n_rows, int32_t C, const int64_t* dst_rows,
+                             int64_t dst_start, uint8_t* codes, uint8_t* scales, int64_t cap_rows, void* stream) {
+  if (!valid_fmt(fmt)) return fail(FP4KV_ERR_UNSUPPORTED, "kv_append: format %d (0, 1 or 2 implemented)", fmt);
+  if (!src || !codes || (fmt != FP4KV_KV_FP8 && !scales))
+    return fail(FP4KV_ERR_NULL, "kv_append: src, codes and (except for FP8) scales must be non-NULL");
+  if (C <= 0 || C % 32 != 0) return fail(FP4KV_ERR_SHAPE, "kv_append: C=%d must be a positive multiple of 32", C);
+  if (n_rows < 0 || cap_rows < 0) return fail(FP4KV_ERR_SHAPE, "kv_append: n_rows and cap_rows must be >= 0");
+  if (!dst_rows && (dst_start < 0 || dst_start + n_rows > cap_rows))
+    return fail(FP4KV_ERR_SHAPE, "kv_append: rows [%lld, %lld) outside the cache of %lld rows",
+                (long long)dst_start, (long long)(dst_start + n_rows), (long long)cap_rows);
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(codes) & 7u))
+    return fail(FP4KV_ERR_SHAPE, "kv_append: src must be 16-byte and codes 8-byte aligned");
+  if (n_rows == 0) return ok();
+  return hip_status(fp4kv::launch_quantize_append(fmt, src, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows,
+                                                  static_cast<hipStream_t>(stream)),
+                    "kv_append");
+}
+
 fp4kv_status fp4kv_quantize_append(const void* src, int64_t n_rows, int32_t C, const int64_t* dst_rows,
                                    int64_t dst_start, uint8_t* codes, uint8_t* scales, int64_t cap_rows,
                                    void* stream) {
-  if (!src || !codes || !scales) return fail(FP4KV_ERR_NULL, "quantize_append: src, codes and scales must be non-NULL");
-  if (C <= 0 || C % 32 != 0) return fail(FP4KV_ERR_SHAPE, "quantize_append: C=%d must be a positive multiple of 32", C);
-  if (n_rows < 0 || cap_rows < 0) return fail(FP4KV_ERR_SHAPE, "quantize_append: n_rows and cap_rows must be >= 0");
-  if (!dst_rows && (dst_start < 0 || dst_start + n_rows > cap_rows))
-    return fail(FP4KV_ERR_SHAPE, "quantize_append: rows [%lld, %lld) outside the cache of %lld rows",
-                (long long)dst_start, (long long)(dst_start + n_rows), (long long)cap_rows);
-  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(codes) & 7u))
-    return fail(FP4KV_ERR_SHAPE, "quantize_append: src must be 16-byte and codes 8-byte aligned");
-  if (n_rows == 0) return ok();
-  return hip_status(fp4kv::launch_quantize_append(src, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows,
-                                                  static_cast<hipStream_t>(stream)),
-                    "quantize_append");
+  return fp4kv_kv_append(FP4KV_KV_FP4, src, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows, stream);
 }
 
 size_t fp4kv_index_workspace_bytes(int32_t n_q, int64_t max_ctx, int32_t block) {
@@ -252,11 +271,13 @@ fp4kv_status fp4kv_index_reindex(const void* idx_q, const float* w, const void* 
   return hip_status(fp4kv::launch_select(se, n_q, true, s), "index_reindex select");
 }
 
-static fp4kv_status check_attn(const char* fn, const void* q, const uint8_t* codes, const uint8_t* scales,
-                               const int32_t* idx, const int32_t* n_idx, const void* swa_k, const void* swa_v,
-                               int32_t nq, int32_t Hq, int32_t C, int32_t k, int32_t W, float scale, const float* out,
-                               void* workspace, size_t ws_bytes) {
-  if (!q || !codes || !scales || !idx || !n_idx || !swa_k || !swa_v || !out)
+static fp4kv_status check_attn(const char* fn, int32_t fmt, const void* q, const uint8_t* codes,
+                               const uint8_t* scales, const int32_t* idx, const int32_t* n_idx, const void* swa_k,
+                               const void* swa_v, int32_t nq, int32_t Hq, int32_t C, int32_t k, int32_t W, float scale,
+                               const float* out, void* workspace, size_t ws_bytes) {
+  if (!valid_fmt(fmt)) return fail(FP4KV_ERR_UNSUPPORTED, "%s: format %d (0, 1 or 2 implemented)", fn, fmt);
+  if (fmt == FP4KV_KV_FP8) scales = nullptr;       // not read
+  if (!q || !codes || (fmt != FP4KV_KV_FP8 && !scales) || !idx || !n_idx || !swa_k || !swa_v || !out)
     return fail(FP4KV_ERR_NULL, "%s: a required pointer is NULL", fn);
   if (nq < 0 || Hq <= 0 || C <= 0 || k < 1 || W < 1 || k > 16384 || W > 16384)
     return fail(FP4KV_ERR_SHAPE, "%s: n_q=%d Hq=%d C=%d k=%d W=%d out of range", fn, nq, Hq, C, k, W);
@@ -273,12 +294,13 @@ static fp4kv_status check_attn(const char* fn, const void* q, const uint8_t* cod
   return FP4KV_OK;
 }
 
-fp4kv_status fp4kv_sparse_attn_decode(const void* q, const uint8_t* codes, const uint8_t* scales, int64_t total_rows,
-                                      const int64_t* seq_start, const int32_t* idx, const int32_t* n_idx,
-                                      const void* swa_k, const void* swa_v, const int32_t* q_pos, int32_t B,
-                                      int32_t Hq, int32_t C, int32_t k, int32_t W, float scale, float* out, float* lse,
-                                      void* workspace, size_t ws_bytes, void* stream) {
-  fp4kv_status st = check_attn("sparse_attn_decode", q, codes, scales, idx, n_idx, swa_k, swa_v, B, Hq, C, k, W,
+fp4kv_status fp4kv_sparse_attn_decode_kv(int32_t fmt, const void* q, const uint8_t* codes, const uint8_t* scales,
+                                         int64_t total_rows, const int64_t* seq_start, const int32_t* idx,
+                                         const int32_t* n_idx, const void* swa_k, const void* swa_v,
+                                         const int32_t* q_pos, int32_t B, int32_t Hq, int32_t C, int32_t k, int32_t W,
+                                         float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+  fp4kv_status st = check_attn("sparse_attn_decode", fmt, q, codes, scales, idx, n_idx, swa_k, swa_v, B, Hq, C, k, W,
                                scale, out, workspace, ws_bytes);
   if (st != FP4KV_OK) return st;
   if (!seq_start || !q_pos) return fail(FP4KV_ERR_NULL, "sparse_attn_decode: seq_start and q_pos must be non-NULL");
@@ -287,6 +309,7 @@ fp4kv_status fp4kv_sparse_attn_decode(const void* q, const uint8_t* codes, const
   a.q = static_cast<const uint16_t*>(q);
   a.codes = codes;
   a.scales = scales;
+  a.kv_fmt = fmt;
   a.total_rows = total_rows;
   a.seq_start = seq_start;
   a.idx = idx;
@@ -305,12 +328,12 @@ fp4kv_status fp4kv_sparse_attn_decode(const void* q, const uint8_t* codes, const
   return hip_status(fp4kv::launch_attn(a, workspace, static_cast<hipStream_t>(stream)), "sparse_attn_decode");
 }
 
-fp4kv_status fp4kv_sparse_attn_prefill(const void* q, const uint8_t* codes, const uint8_t* scales, int64_t total_rows,
-                                       int64_t seq_start, const int32_t* idx, const int32_t* n_idx, const void* swa_k,
-                                       const void* swa_v, int32_t pos0, int32_t T, int32_t Hq, int32_t C, int32_t k,
-                                       int32_t W, float scale, float* out, float* lse, void* workspace,
-                                       size_t ws_bytes, void* stream) {
-  fp4kv_status st = check_attn("sparse_attn_prefill", q, codes, scales, idx, n_idx, swa_k, swa_v, T, Hq, C, k, W,
+fp4kv_status fp4kv_sparse_attn_prefill_kv(int32_t fmt, const void* q, const uint8_t* codes, const uint8_t* scales,
+                                          int64_t total_rows, int64_t seq_start, const int32_t* idx,
+                                          const int32_t* n_idx, const void* swa_k, const void* swa_v, int32_t pos0,
+                                          int32_t T, int32_t Hq, int32_t C, int32_t k, int32_t W, float scale,
+                                          float* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  fp4kv_status st = check_attn("sparse_attn_prefill", fmt, q, codes, scales, idx, n_idx, swa_k, swa_v, T, Hq, C, k, W,
                                scale, out, workspace, ws_bytes);
   if (st != FP4KV_OK) return st;
   if (pos0 < 0 || seq_start < 0) return fail(FP4KV_ERR_SHAPE, "sparse_attn_prefill: pos0 and seq_start must be >= 0");
@@ -319,6 +342,7 @@ fp4kv_status fp4kv_sparse_attn_prefill(const void* q, const uint8_t* codes, cons
   a.q = static_cast<const uint16_t*>(q);
   a.codes = codes;
   a.scales = scales;
+  a.kv_fmt = fmt;
   a.total_rows = total_rows;
   a.seq_start = nullptr;
   a.seq_start_scalar = seq_start;
@@ -337,6 +361,24 @@ fp4kv_status fp4kv_sparse_attn_prefill(const void* q, const uint8_t* codes, cons
   a.out = out;
   a.lse = lse;
   return hip_status(fp4kv::launch_attn(a, workspace, static_cast<hipStream_t>(stream)), "sparse_attn_prefill");
+}
+
+fp4kv_status fp4kv_sparse_attn_decode(const void* q, const uint8_t* codes, const uint8_t* scales, int64_t total_rows,
+                                      const int64_t* seq_start, const int32_t* idx, const int32_t* n_idx,
+                                      const void* swa_k, const void* swa_v, const int32_t* q_pos, int32_t B,
+                                      int32_t Hq, int32_t C, int32_t k, int32_t W, float scale, float* out, float* lse,
+                                      void* workspace, size_t ws_bytes, void* stream) {
+  return fp4kv_sparse_attn_decode_kv(FP4KV_KV_FP4, q, codes, scales, total_rows, seq_start, idx, n_idx, swa_k, swa_v,
+                                     q_pos, B, Hq, C, k, W, scale, out, lse, workspace, ws_bytes, stream);
+}
+
+fp4kv_status fp4kv_sparse_attn_prefill(const void* q, const uint8_t* codes, const uint8_t* scales, int64_t total_rows,
+                                       int64_t seq_start, const int32_t* idx, const int32_t* n_idx, const void* swa_k,
+                                       const void* swa_v, int32_t pos0, int32_t T, int32_t Hq, int32_t C, int32_t k,
+                                       int32_t W, float scale, float* out, float* lse, void* workspace,
+                                       size_t ws_bytes, void* stream) {
+  return fp4kv_sparse_attn_prefill_kv(FP4KV_KV_FP4, q, codes, scales, total_rows, seq_start, idx, n_idx, swa_k,
+                                      swa_v, pos0, T, Hq, C, k, W, scale, out, lse, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

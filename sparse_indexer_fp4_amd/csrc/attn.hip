@@ -87,8 +87,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // both kinds (merging the two would copy registers that are still being
 // loaded, which waits for the loads).
 struct RawSparse {
-  uint32_t code[4];   // channels 8c..8c+7 of row r (a stand-in row where row r is not real)
-  uint32_t scale[4];  // the row's aligned scale word holding these channels' scale byte (likewise)
+  // Channels 8c..8c+7 of row r (a stand-in row where row r is not real):
+  //   FP4 and MXFP4: code = their 8 nibbles, scale = the row's aligned scale word
+  //                  holding their scale byte;
+  //   FP8:           code = the E4M3 bytes of channels 8c..8c+3, scale = of 8c+4..8c+7.
+  uint32_t code[4];
+  uint32_t scale[4];
   uint32_t valid;     // bit r: row r is real; the others are zeroed when committed
 };
 struct RawWindow {
@@ -155,7 +159,7 @@ __device__ __forceinline__ int64_t chunk_pos(const AttnArgs& a, int qi, int m, i
 // scales of a sparse chunk, or bf16 keys and values of a window chunk. The
 // registers are not read until the chunk is committed, so the loads stay in
 // flight while the current chunk is computed.
-template <int NHG>
+template <int NHG, int FMT>
 __device__ __forceinline__ void load_sparse(const AttnArgs& a, const QueryInfo& Q, int qi, int c, int m, int idxv,
                                             RawSparse (&raw)[kItems / (128 * NHG)]) {
   constexpr int PER = kItems / (128 * NHG);
@@ -169,8 +173,16 @@ __device__ __forceinline__ void load_sparse(const AttnArgs& a, const QueryInfo& 
       const int j = c * kChunk + 4 * rg + r;
       const int64_t row = sparse_row(a, Q, j, chunk_pos<NHG>(a, qi, m, j, it, r, idxv));
       const int64_t rr = row < 0 ? 0 : row;
-      raw[it].code[r] = *reinterpret_cast<const uint32_t*>(a.codes + rr * (kAttnC / 2) + 4 * cg);
-      raw[it].scale[r] = *reinterpret_cast<const uint32_t*>(a.scales + rr * (kAttnC / 16) + 4 * (cg >> 3));
+      if constexpr (FMT == kKvFp8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(a.codes + rr * kAttnC + 8 * cg);
+        raw[it].code[r] = v.x;
+        raw[it].scale[r] = v.y;
+      } else {
+        constexpr int kGroupShift = FMT == kKvMxfp4 ? 2 : 1;     // items (8 channels) per scale byte: 4 or 2
+        raw[it].code[r] = *reinterpret_cast<const uint32_t*>(a.codes + rr * (kAttnC / 2) + 4 * cg);
+        raw[it].scale[r] = *reinterpret_cast<const uint32_t*>(
+            a.scales + rr * (kAttnC / (8 << kGroupShift)) + 4 * (cg >> (kGroupShift + 2)));
+      }
       bits |= (uint32_t)(row >= 0) << r;
     }
     raw[it].valid = bits;
@@ -206,7 +218,16 @@ __device__ __forceinline__ void store_rows(uint4* buf, int rg, int cg, const uin
   for (int r = 0; r < 4; ++r) buf[kbuf_unit(4 * rg + r, cg)] = make_uint4(d[r][0], d[r][1], d[r][2], d[r][3]);
 }
 
-template <int NHG>
+// bf16 pair (lo, hi) of two E4M3FN codes, exact: a normal code's fields move
+// into an fp32, a subnormal one (m * 2^-9) is formed by a product. (The NaN
+// codes 0x7F and 0xFF are never written by the append and decode as 480.)
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
+}
+
+template <int NHG, int FMT>
 __device__ __forceinline__ void commit_sparse(AttnShared<NHG>& sh, const RawSparse (&raw)[kItems / (128 * NHG)]) {
   constexpr int PER = kItems / (128 * NHG);
 #pragma unroll
@@ -216,23 +237,42 @@ __device__ __forceinline__ void commit_sparse(AttnShared<NHG>& sh, const RawSpar
     const uint32_t valid = raw[it].valid;
     if (cg == 0) sh.vb[rg] = valid;
     uint32_t d[4][4];
-    // twice the E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 as bytes
-    constexpr uint32_t lut_lo = 0x03020100u, lut_hi = 0x0C080604u;
+    if constexpr (FMT == kKvFp8) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool real = (valid >> r) & 1u;
-      const uint32_t code = real ? raw[it].code[r] : 0u;
-      const float sh2 = e4m3_half(real ? (raw[it].scale[r] >> (8 * ((cg >> 1) & 3))) & 0xFFu : 0u);
-      const uint32_t me = __builtin_amdgcn_perm(lut_hi, lut_lo, code & 0x07070707u);         // even channels
-      const uint32_t mo = __builtin_amdgcn_perm(lut_hi, lut_lo, (code >> 4) & 0x07070707u);  // odd channels
+      for (int r = 0; r < 4; ++r) {
+        const bool real = (valid >> r) & 1u;
+        const uint32_t lo = real ? raw[it].code[r] : 0u, hi = real ? raw[it].scale[r] : 0u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float f0 = (float)((me >> (8 * j)) & 0xFFu) * sh2;
-        float f1 = (float)((mo >> (8 * j)) & 0xFFu) * sh2;
-        // sign bits of nibbles 2j (bit 8j+3) and 2j+1 (bit 8j+7)
-        f0 = __uint_as_float(__float_as_uint(f0) | ((code << (28 - 8 * j)) & 0x80000000u));
-        f1 = __uint_as_float(__float_as_uint(f1) | ((code << (24 - 8 * j)) & 0x80000000u));
-        d[r][j] = pack_bf16x2(f0, f1);
+        for (int j = 0; j < 2; ++j) {
+          d[r][j] = pack_bf16x2(e4m3_to_f32((lo >> (16 * j)) & 0xFFu), e4m3_to_f32((lo >> (16 * j + 8)) & 0xFFu));
+          d[r][2 + j] = pack_bf16x2(e4m3_to_f32((hi >> (16 * j)) & 0xFFu), e4m3_to_f32((hi >> (16 * j + 8)) & 0xFFu));
+        }
+      }
+    } else {
+      // twice the E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 as bytes
+      constexpr uint32_t lut_lo = 0x03020100u, lut_hi = 0x0C080604u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool real = (valid >> r) & 1u;
+        const uint32_t code = real ? raw[it].code[r] : 0u;
+        float sh2;   // half the block scale (the table holds twice the magnitudes)
+        if constexpr (FMT == kKvMxfp4) {
+          const uint32_t sc = (raw[it].scale[r] >> (8 * ((cg >> 2) & 3))) & 0xFFu;
+          sh2 = real ? __builtin_ldexpf(1.0f, (int)sc - 128) : 0.0f;   // 2^(sc - 127) / 2, exact
+        } else {
+          sh2 = e4m3_half(real ? (raw[it].scale[r] >> (8 * ((cg >> 1) & 3))) & 0xFFu : 0u);
+        }
+        const uint32_t me = __builtin_amdgcn_perm(lut_hi, lut_lo, code & 0x07070707u);         // even channels
+        const uint32_t mo = __builtin_amdgcn_perm(lut_hi, lut_lo, (code >> 4) & 0x07070707u);  // odd channels
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float f0 = (float)((me >> (8 * j)) & 0xFFu) * sh2;
+          float f1 = (float)((mo >> (8 * j)) & 0xFFu) * sh2;
+          // sign bits of nibbles 2j (bit 8j+3) and 2j+1 (bit 8j+7)
+          f0 = __uint_as_float(__float_as_uint(f0) | ((code << (28 - 8 * j)) & 0x80000000u));
+          f1 = __uint_as_float(__float_as_uint(f1) | ((code << (24 - 8 * j)) & 0x80000000u));
+          d[r][j] = pack_bf16x2(f0, f1);
+        }
       }
     }
     store_rows(sh.kbuf, rg, cg, d);
@@ -268,7 +308,7 @@ __device__ __forceinline__ void commit_window(AttnShared<NHG>& sh, const RawWind
 // of the 512 output channels (64 accumulators per lane, so two waves fit on a
 // SIMD). The two waves of a head group each form S over their half of the
 // channels and exchange the partial sums through LDS.
-template <int NHG>
+template <int NHG, int FMT>
 __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   constexpr int PER = kItems / (128 * NHG);
   __shared__ AttnShared<NHG> sh;
@@ -303,7 +343,7 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   const int nW = nT - nS, w0 = nW > 0 ? 1 : 0;
   RawSparse rs[PER];
   RawWindow rw[PER];
-  if (nS > 0) load_sparse<NHG>(a, Q, qi, split, 0, idxv, rs);
+  if (nS > 0) load_sparse<NHG, FMT>(a, Q, qi, split, 0, idxv, rs);
   // (with several items per thread the window slot would not fit in registers
   // beside the accumulators: the first window chunk is then loaded at commit)
   if constexpr (PER == 1) {
@@ -340,14 +380,14 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
         commit_window<NHG>(sh, tw);
       }
     } else if (i < nS) {
-      commit_sparse<NHG>(sh, rs);
+      commit_sparse<NHG, FMT>(sh, rs);
     } else {
       RawWindow tw[PER];
       load_window<NHG>(a, Q, split + (i + 1) * ns_, tw);   // window ordinal i - nS + 1
       commit_window<NHG>(sh, tw);
     }
     __syncthreads();
-    if (step >= w0 && i + 1 < nS) load_sparse<NHG>(a, Q, qi, split + (i + 1) * ns_, i + 1, idxv, rs);
+    if (step >= w0 && i + 1 < nS) load_sparse<NHG, FMT>(a, Q, qi, split + (i + 1) * ns_, i + 1, idxv, rs);
 
     // partial S^T over this channel half: A = even rows (tile 0) / odd rows (tile 1), B = Q^T
     v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -504,12 +544,14 @@ hipError_t launch_attn(AttnArgs a, void* ws, hipStream_t stream) {
   }
   const int nhg = a.Hq / 16;
   dim3 grid((uint32_t)a.n_split, (uint32_t)a.nq);
-  switch (nhg) {
-    case 1: attn_kernel<1><<<grid, dim3(128), 0, stream>>>(a); break;
-    case 2: attn_kernel<2><<<grid, dim3(256), 0, stream>>>(a); break;
-    case 4: attn_kernel<4><<<grid, dim3(512), 0, stream>>>(a); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (a.kv_fmt < kKvFp4 || a.kv_fmt > kKvFp8) return hipErrorInvalidValue;
+#define FP4KV_ATTN_CASE(NH, FM) \
+  if (nhg == NH && a.kv_fmt == FM) attn_kernel<NH, FM><<<grid, dim3(128 * NH), 0, stream>>>(a); else
+  FP4KV_ATTN_CASE(1, kKvFp4) FP4KV_ATTN_CASE(2, kKvFp4) FP4KV_ATTN_CASE(4, kKvFp4)
+  FP4KV_ATTN_CASE(1, kKvMxfp4) FP4KV_ATTN_CASE(2, kKvMxfp4) FP4KV_ATTN_CASE(4, kKvMxfp4)
+  FP4KV_ATTN_CASE(1, kKvFp8) FP4KV_ATTN_CASE(2, kKvFp8) FP4KV_ATTN_CASE(4, kKvFp8)
+  return hipErrorInvalidValue;
+#undef FP4KV_ATTN_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const dim3 cgrid((uint32_t)a.Hq, (uint32_t)a.nq);

@@ -5,6 +5,13 @@
 
 namespace fp4kv {
 
+// Main-KV storage formats (values of the ABI's format argument).
+enum KvFmt : int32_t {
+  kKvFp4 = 0,     // E2M1 codes + one E4M3 scale per 16 channels
+  kKvMxfp4 = 1,   // E2M1 codes + one E8M0 scale per 32 channels
+  kKvFp8 = 2,     // one E4M3FN code per channel, no scale
+};
+
 struct ScanArgs {
   const uint16_t* idx_q;     // [n_q, H, D] bf16
   const float* w;            // [n_q, H]
@@ -55,8 +62,9 @@ struct SelectArgs {
 
 struct AttnArgs {
   const uint16_t* q;              // [nq, Hq, C] bf16
-  const uint8_t* codes;           // [total_rows, C/2]
-  const uint8_t* scales;          // [total_rows, C/16]
+  const uint8_t* codes;           // [total_rows, C/2] (FP8: [total_rows, C])
+  const uint8_t* scales;          // [total_rows, C/16] (MXFP4: C/32; FP8: unused)
+  int32_t kv_fmt;                 // KvFmt
   int64_t total_rows;
   const int64_t* seq_start;       // [nq] (decode) or nullptr (prefill: seq_start_scalar)
   int64_t seq_start_scalar;
@@ -78,9 +86,9 @@ struct AttnArgs {
   float* part_ml;                 // [nq, n_split, Hq, 2]
 };
 
-hipError_t launch_quantize_append(const void* src, int64_t n_rows, int32_t C, const int64_t* dst_rows,
-                                  int64_t dst_start, uint8_t* codes, uint8_t* scales, int64_t cap_rows,
-                                  hipStream_t stream);
+hipError_t launch_quantize_append(int32_t fmt, const void* src, int64_t n_rows, int32_t C,
+                                  const int64_t* dst_rows, int64_t dst_start, uint8_t* codes, uint8_t* scales,
+                                  int64_t cap_rows, hipStream_t stream);
 bool scan_supported(int H, int D);
 // slots: max_ctx for a Full scan, P*8 for a Reindex scan.
 hipError_t launch_scan(ScanArgs a, int H, int D, int n_q, int64_t slots, bool reindex, hipStream_t stream);

@@ -1,5 +1,8 @@
-// FP4 quantize-append: E2M1 values with one E4M3 scale per 16 channels.
-// [G] FP4 main KV paragraph; [N] "FP4 KV Quantization and Cache Lifetime Management".
+// Main-KV quantize-append. The FP4 cache: E2M1 values with one E4M3 scale per
+// 16 channels ([G] FP4 main KV paragraph; [N] "FP4 KV Quantization and Cache
+// Lifetime Management"). Two variants for the formats the pages compare it with:
+// MXFP4, E2M1 with one E8M0 scale per 32 channels ([T] "Mechanism 3"), and an
+// FP8 cache of E4M3FN codes ([G], [N]: FP4 is about half its bytes).
 //
 // One thread per 16-channel group. Rounding decisions are taken by exact
 // comparisons, never by rounding a quotient:
@@ -101,13 +104,124 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
   scales[dst * G + g] = (uint8_t)sc;
 }
 
-hipError_t launch_quantize_append(const void* src, int64_t n_rows, int32_t C, const int64_t* dst_rows,
-                                  int64_t dst_start, uint8_t* codes, uint8_t* scales, int64_t cap_rows,
-                                  hipStream_t stream) {
-  const int64_t n = n_rows * (C >> 4);
-  const int64_t blocks = (n + 255) / 256;
-  quantize_append_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
-      static_cast<const uint16_t*>(src), n_rows, C, dst_rows, dst_start, codes, scales, cap_rows);
+// ---- MXFP4: one thread per 32-channel block.
+
+// Shared exponent of an MX block from the fp32 bits of its amax (a bf16 value):
+// floor(log2 amax) - 2, clamped to [-127, 127]; -127 for amax = 0. Subnormal
+// amax (value = bits * 2^-149) takes floor(log2) from its leading bit.
+__device__ __forceinline__ int mx_shared_exp(uint32_t amax_bits) {
+  if (amax_bits == 0u) return -127;
+  const int e = (int)(amax_bits >> 23);
+  const int fl = e > 0 ? e - 127 : -149 + (31 - (int)__clz(amax_bits));
+  const int sh = fl - 2;
+  return sh < -127 ? -127 : (sh > 127 ? 127 : sh);
+}
+
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(
+    const uint16_t* __restrict__ src, int64_t n_rows, int32_t C, const int64_t* __restrict__ dst_rows,
+    int64_t dst_start, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t cap_rows) {
+  const int32_t G = C >> 5;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n_rows * G) return;
+  const int64_t row = gid / G;
+  const int32_t g = (int32_t)(gid - row * G);
+  const int64_t dst = dst_rows ? dst_rows[row] : dst_start + row;
+  if (dst < 0 || dst >= cap_rows) return;
+
+  const uint4* p = reinterpret_cast<const uint4*>(src + row * C + g * 32);
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = p[i];
+    w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax_bits = max(amax_bits, max((w[i] << 16) & 0x7FFF0000u, w[i] & 0x7FFF0000u));
+  const int sh = mx_shared_exp(amax_bits);
+  // 2^-sh is a normal float: sh <= 125 for any finite bf16 amax (< 2^128)
+  const float inv = __uint_as_float((uint32_t)(127 - sh) << 23);
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    // x * 2^-sh is exact (power of two; |result| < 8), and keeps the sign bit
+    const uint32_t c0 = encode_value(__uint_as_float(w[i] << 16) * inv, 1.0f);
+    const uint32_t c1 = encode_value(__uint_as_float(w[i] & 0xFFFF0000u) * inv, 1.0f);
+    out[i >> 2] |= (c0 | (c1 << 4)) << (8 * (i & 3));
+  }
+  uint2* q = reinterpret_cast<uint2*>(codes + dst * (C >> 1) + g * 16);
+  q[0] = make_uint2(out[0], out[1]);
+  q[1] = make_uint2(out[2], out[3]);
+  scales[dst * G + g] = (uint8_t)(sh + 127);
+}
+
+// ---- FP8: one thread per 16 channels.
+
+// E4M3FN code of x: the nearest finite value, ties to the even code, saturating
+// at 448; sign bit = sign bit of x. x is a bf16 value (at most 8 significant
+// bits), so the rounding is decided exactly on its bits.
+__device__ __forceinline__ uint32_t encode_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float ax = fabsf(x);
+  uint32_t c;
+  if (ax > 448.0f) {
+    c = 126u;
+  } else if (ax < 0.015625f) {             // below 2^-6: subnormal step 2^-9 (the product is exact)
+    c = (uint32_t)__builtin_rintf(ax * 512.0f);
+  } else {
+    const uint32_t b = __float_as_uint(ax);
+    const uint32_t e = (b >> 23) - 120u;   // biased E4M3 exponent: (e32 - 127) + 7
+    const uint32_t m = (b >> 20) & 7u, rest = b & 0xFFFFFu;
+    const uint32_t up = (rest > 0x80000u) | ((rest == 0x80000u) & (m & 1u));
+    c = (e << 3) + m + up;                 // a carry moves into the exponent; <= 126 since ax <= 448
+  }
+  return sign | c;
+}
+
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(
+    const uint16_t* __restrict__ src, int64_t n_rows, int32_t C, const int64_t* __restrict__ dst_rows,
+    int64_t dst_start, uint8_t* __restrict__ codes, int64_t cap_rows) {
+  const int32_t G = C >> 4;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n_rows * G) return;
+  const int64_t row = gid / G;
+  const int32_t g = (int32_t)(gid - row * G);
+  const int64_t dst = dst_rows ? dst_rows[row] : dst_start + row;
+  if (dst < 0 || dst >= cap_rows) return;
+  const uint4* p = reinterpret_cast<const uint4*>(src + row * C + g * 16);
+  const uint4 v0 = p[0], v1 = p[1];
+  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = encode_e4m3(__uint_as_float(w[2 * i] << 16));
+    const uint32_t b = encode_e4m3(__uint_as_float(w[2 * i] & 0xFFFF0000u));
+    const uint32_t c = encode_e4m3(__uint_as_float(w[2 * i + 1] << 16));
+    const uint32_t d = encode_e4m3(__uint_as_float(w[2 * i + 1] & 0xFFFF0000u));
+    out[i] = a | (b << 8) | (c << 16) | (d << 24);
+  }
+  uint2* q = reinterpret_cast<uint2*>(codes + dst * C + g * 16);
+  q[0] = make_uint2(out[0], out[1]);
+  q[1] = make_uint2(out[2], out[3]);
+}
+
+hipError_t launch_quantize_append(int32_t fmt, const void* src, int64_t n_rows, int32_t C,
+                                  const int64_t* dst_rows, int64_t dst_start, uint8_t* codes, uint8_t* scales,
+                                  int64_t cap_rows, hipStream_t stream) {
+  const uint16_t* s16 = static_cast<const uint16_t*>(src);
+  if (fmt == kKvMxfp4) {
+    const int64_t n = n_rows * (C >> 5);
+    quantize_mxfp4_kernel<<<dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream>>>(
+        s16, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows);
+  } else if (fmt == kKvFp8) {
+    const int64_t n = n_rows * (C >> 4);
+    quantize_fp8_kernel<<<dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream>>>(
+        s16, n_rows, C, dst_rows, dst_start, codes, cap_rows);
+  } else {
+    const int64_t n = n_rows * (C >> 4);
+    quantize_append_kernel<<<dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream>>>(
+        s16, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows);
+  }
   return hipGetLastError();
 }
 

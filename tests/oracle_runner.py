@@ -8,7 +8,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from oracle import attention, fp4, indexer
+from oracle import attention, fp4, indexer, kvformats
 from synth import bf16_to_f64
 from synth import workloads as wl
 
@@ -35,18 +35,24 @@ def reindex_layer(cfg, i, layer, pool):
     return indexer.index_reindex(bf16_to_f64(q), w.numpy().astype(np.float64), rows_of, pool, p, cfg.k)
 
 
-def dequantized_rows(cfg, s, positions):
+def dequantized_rows(cfg, s, positions, fmt=kvformats.FMT_FP4):
+    """Main-KV rows at `positions` as the cache in format fmt holds them; fmt None
+    gives the unquantised bf16 rows."""
     x = bf16_to_f64(wl.kv_rows(cfg, s, torch.from_numpy(np.asarray(positions, dtype=np.int64))))
-    codes, scales = fp4.quantize_rows(x)
-    return fp4.dequantize_rows(codes, scales)
+    if fmt is None:
+        return x
+    if fmt == kvformats.FMT_FP4:
+        return fp4.dequantize_rows(*fp4.quantize_rows(x))
+    return kvformats.dequantize_rows(fmt, *kvformats.quantize_rows(fmt, x))
 
 
-def attend(cfg, i, layer, idx):
-    """(out [Hq, C], lse [Hq]) of query i in `layer`, attending to positions idx."""
+def attend(cfg, i, layer, idx, fmt=kvformats.FMT_FP4):
+    """(out [Hq, C], lse [Hq]) of query i in `layer`, attending to positions idx
+    of a main-KV cache in format fmt (None: unquantised rows)."""
     s = wl.sequence_of(cfg, i)
     p = int(cfg.q_pos()[i])
     Q = bf16_to_f64(wl.main_query(cfg, layer, i))
-    rows = dequantized_rows(cfg, s, idx) if len(idx) else np.zeros((0, cfg.C))
+    rows = dequantized_rows(cfg, s, idx, fmt) if len(idx) else np.zeros((0, cfg.C))
     wpos = torch.arange(max(0, p - cfg.W + 1), p + 1, dtype=torch.int64)
     wk = bf16_to_f64(wl.window_rows(cfg, layer, s, wpos, "k"))
     wv = bf16_to_f64(wl.window_rows(cfg, layer, s, wpos, "v"))

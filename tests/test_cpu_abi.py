@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib.lib, n), n
     assert sorted(lib.EXPORTS) == names
@@ -64,3 +64,23 @@ def test_workspace_sizes(lib):
     assert lib.fp4kv_reindex_workspace_bytes(8, 2048) >= 8 * 2048 * 8 * 4
     assert lib.fp4kv_attn_workspace_bytes(4096, 64, 512, 512, 128) == 0   # one split when queries fill the GPU
     assert lib.fp4kv_attn_workspace_bytes(1, 64, 512, 512, 128) > 0
+
+
+def test_kv_format_sizes_and_checks_without_gpu(lib):
+    """Row bytes per main-KV format; unknown formats are refused; an FP8 cache
+    needs no scale plane. Nothing is launched (zero rows or queries)."""
+    L = lib.lib
+    assert [L.fp4kv_kv_code_bytes(f, 512) for f in (0, 1, 2)] == [256, 256, 512]
+    assert [L.fp4kv_kv_scale_bytes(f, 512) for f in (0, 1, 2)] == [32, 16, 0]
+    assert L.fp4kv_kv_code_bytes(3, 512) == -1 and L.fp4kv_kv_scale_bytes(1, 48) == -1
+    fake = ctypes.c_void_p(4096)
+    assert L.fp4kv_kv_append(3, fake, 4, 512, None, 0, fake, fake, 4, None) == -4
+    assert L.fp4kv_kv_append(1, fake, 4, 512, None, 0, fake, None, 4, None) == -1     # MXFP4 needs scales
+    assert L.fp4kv_kv_append(2, fake, 0, 512, None, 0, fake, None, 4, None) == 0      # FP8: no scale plane
+    assert L.fp4kv_kv_append(1, fake, 4, 64, None, 2, fake, fake, 4, None) == -2      # rows past the cache
+    # q, codes, scales = NULL, total_rows, seq_start, idx, n_idx, swa_k, swa_v, q_pos, B = 0, Hq, C, k, W, ...
+    a = [fake, fake, None, 100, fake, fake, fake, fake, fake, fake, 0, 64, 512, 8, 128, ctypes.c_float(0.1), fake,
+         None, fake, 1 << 30, None]
+    assert L.fp4kv_sparse_attn_decode_kv(2, *a) == 0                        # FP8, no queries, no scale plane
+    assert L.fp4kv_sparse_attn_decode_kv(1, *a) == -1                       # MXFP4 needs scales
+    assert L.fp4kv_sparse_attn_decode_kv(5, *a) == -4
