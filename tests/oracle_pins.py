@@ -20,7 +20,7 @@ import numpy as np
 import scipy.special
 import torch
 
-from oracle import attention, chain, fp4, indexer, kvformats
+from oracle import attention, chain, fp4, indexer, kvformats, paged
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -288,6 +288,59 @@ def check_kv_format_bytes():
     b = [kvformats.bytes_per_row(f, C) for f in (kvformats.FMT_FP4, kvformats.FMT_MXFP4, kvformats.FMT_FP8)]
     assert b == [288, 272, 512] and b[0] == fp4.bytes_per_row(C)
     assert abs(b[0] / b[2] - c["fp4_over_fp8_approx"]) < 0.1
+
+
+# ------------------------------------------------- paged cache and ring ----
+
+def check_paged_worked_example():
+    """Hand-worked mapping with pages of 4 rows: sequence 1's block table
+    [5, 2, -1]; position 6 is page 1 (physical page 2), offset 2 -> row 10;
+    position 3 -> page 5 -> row 23; position 9 is page 2, which maps nowhere;
+    a page id past n_pages (7 >= 6) maps nowhere too."""
+    bt = np.array([[0, 1, 3], [5, 2, -1], [7, 4, 4]])
+    assert paged.physical_row(bt, 4, 6, 1, 6) == 10
+    assert paged.physical_row(bt, 4, 6, 1, 3) == 23
+    assert paged.physical_row(bt, 4, 6, 1, 9) == -1
+    assert paged.physical_row(bt, 4, 6, 2, 1) == -1
+    assert paged.physical_row(bt, 4, 6, 0, 12) == -1          # past the table
+    assert paged.physical_row(bt, 4, 6, 0, -1) == -1
+
+
+def check_paged_round_trip():
+    """With a random permutation of physical pages as the block tables, every
+    position of every sequence has its own physical row, and reading a sequence
+    back through the table gives its rows in order (the storage is transparent)."""
+    rng = np.random.default_rng(3)
+    page, lengths = 64, [130, 64, 1, 300]
+    need = [-(-n // page) for n in lengths]
+    perm = rng.permutation(sum(need) + 3)
+    bt = np.full((len(lengths), max(need)), -1)
+    k = 0
+    for s, n in enumerate(need):
+        bt[s, :n] = perm[k:k + n]; k += n
+    n_pages = sum(need) + 3
+    rows = [rng.integers(-100, 100, (n, 5)) for n in lengths]
+    store = paged.paged_store(rows, bt, page, n_pages, fill=12345)
+    seen = set()
+    for s, n in enumerate(lengths):
+        phys = [paged.physical_row(bt, page, n_pages, s, t) for t in range(n)]
+        assert min(phys) >= 0 and not (seen & set(phys)); seen |= set(phys)
+        assert np.array_equal(paged.logical_rows(store, bt, page, n_pages, s, np.arange(n)), rows[s])
+    assert (store == 12345).all(axis=1).sum() == n_pages * page - sum(lengths)
+
+
+def check_ring_window():
+    """After appending positions 0..p in order, the ring read for position p gives
+    exactly the last min(W, p+1) rows, oldest first, for p below, at and far past W."""
+    # the layout itself (the library's ring buffers follow it): position t in slot t mod W
+    assert [paged.ring_slot(t, 128) for t in (0, 127, 128, 130, 1000)] == [0, 127, 0, 2, 104]
+    rng = np.random.default_rng(4)
+    W = 8
+    for n in (1, 5, 8, 9, 30):
+        rows = rng.integers(0, 1000, (n, 3))
+        ring = paged.ring_after_appends(rows, W)
+        got = paged.window_from_ring(ring, n - 1, W)
+        assert np.array_equal(got, rows[max(0, n - W):n]), n
 
 
 # -------------------------------------------------------------- indexer ----

@@ -6,7 +6,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import attention, chain, fp4, indexer, kvformats
+from oracle import attention, chain, fp4, indexer, kvformats, paged
 from tests import oracle_pins
 
 
@@ -147,6 +147,23 @@ def _fp8_overflow_nan(x):
     return np.where(np.abs(np.asarray(x, float)) > 448.0, c | 0x7F, c).astype(np.uint8)
 
 
+def _page_offset_swapped(block_table, page_rows, n_pages, seq, pos):
+    if pos < 0 or pos // page_rows >= block_table.shape[1]:
+        return -1
+    g = int(block_table[seq, pos // page_rows])
+    return -1 if g < 0 or g >= n_pages else g + (pos % page_rows) * n_pages
+
+
+def _page_no_bounds(block_table, page_rows, n_pages, seq, pos):
+    if pos < 0 or pos // page_rows >= block_table.shape[1]:
+        return -1
+    return int(block_table[seq, pos // page_rows]) * page_rows + pos % page_rows
+
+
+def _ring_slot_off_by_one(pos, W):
+    return (pos + 1) % W
+
+
 MUTANTS = [
     ("scores: no ReLU", indexer, "token_scores", _no_relu),
     ("scores: dropped head", indexer, "token_scores", _drop_last_head),
@@ -172,6 +189,9 @@ MUTANTS = [
     ("FP8 ties upward", kvformats, "fp8_encode", _fp8_ties_up),
     ("FP8 sign dropped", kvformats, "fp8_encode", _fp8_sign_dropped),
     ("FP8 overflow to NaN", kvformats, "fp8_encode", _fp8_overflow_nan),
+    ("page row and page swapped", paged, "physical_row", _page_offset_swapped),
+    ("page ids not bounded", paged, "physical_row", _page_no_bounds),
+    ("ring slot off by one", paged, "ring_slot", _ring_slot_off_by_one),
 ]
 
 
