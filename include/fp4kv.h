@@ -343,6 +343,105 @@ fp4kv_status fp4kv_sparse_attn_prefill_kv(int32_t fmt, const void* q, const uint
                                           float scale, float* out, float* lse, void* workspace,
                                           size_t ws_bytes, void* stream);
 
+/*
+ * Paged cache and window ring: the serving-side storage around the path.
+ * [N] "FP4 KV Quantization and Cache Lifetime Management" (a long-lived global
+ * KV cache, with the window state kept apart from it); [G] SWA Bounded Replay
+ * paragraph and [N] "Causal Encoder-Decoder and Prefill Halving" (each layer's
+ * window is the last 128 tokens). The pages give no layout; this one:
+ *
+ *   Pages. A sequence's positions are cut into pages of page_rows consecutive
+ *   positions (a power of two in [64, 2^20]); page i holds positions
+ *   i*page_rows .. (i+1)*page_rows - 1. block_table (device) int32
+ *   [n_seq, max_pages]: block_table[s*max_pages + i] is the physical page of
+ *   sequence s's page i, and physical page g is rows g*page_rows ..
+ *   (g+1)*page_rows - 1 of every per-token store: main-KV codes and scales (in
+ *   a format of FP4KV_KV_*) and indexer keys, each with n_pages*page_rows rows.
+ *   An entry outside [0, n_pages) maps nowhere.
+ *   Window ring. Per layer, ring_k and ring_v (device) bf16 [n_seq, W, C]:
+ *   position t of sequence s is row s*W + (t mod W). After positions
+ *   0..p have been appended in order it holds the last min(W, p+1) of them.
+ *
+ * The method's results are unchanged by paging: a paged call returns exactly
+ * what the contiguous call returns for the same logical sequences (same bits).
+ * The block table must map every position a call reads (0..q_pos); a page that
+ * maps nowhere is read as row 0 by the indexer and is skipped by attention,
+ * so no access leaves the stores.
+ */
+
+/*
+ * Append new tokens' rows to a paged cache (variable counts per sequence): row
+ * i goes to position row_pos[i] of sequence row_seq[i], i.e. to its physical
+ * row through the block table; rows that map nowhere are not written.
+ *   kv_src    (device) bf16 [n_rows, C] main-KV rows, quantised into (codes,
+ *             scales) in format fmt as fp4kv_kv_append does; or NULL.
+ *   idxk_src  (device) bf16 [n_rows, D] indexer keys, copied into idx_k
+ *             [n_pages*page_rows, D]; or NULL. At least one of the two.
+ *   row_seq   (device) int32 [n_rows]; row_pos (device) int64 [n_rows].
+ * Errors: NULL pointers as required; C (multiple of 32) or D (multiple of 8)
+ * out of range; the page arguments (see above); alignment as for
+ * fp4kv_kv_append (idxk_src and idx_k 16-byte).
+ */
+fp4kv_status fp4kv_paged_kv_append(int32_t fmt, const void* kv_src, const void* idxk_src,
+                                   int64_t n_rows, int32_t C, int32_t D, const int32_t* row_seq,
+                                   const int64_t* row_pos, const int32_t* block_table,
+                                   int32_t n_seq, int32_t max_pages, int32_t page_rows,
+                                   int64_t n_pages, uint8_t* codes, uint8_t* scales, void* idx_k,
+                                   void* stream);
+
+/*
+ * Append window rows to a layer's ring: row i (k_src, v_src (device) bf16
+ * [n_rows, C]) to slot row_pos[i] mod W of sequence row_seq[i]. Rows with a
+ * sequence outside [0, n_seq) or a negative position are not written. Within
+ * one call a sequence's positions must be distinct modulo W (for example at
+ * most W consecutive positions: a prefill chunk appends only its last W rows);
+ * where two rows of a call share a slot, which one the slot keeps is not
+ * specified. C a positive multiple of 8; every buffer 16-byte aligned.
+ */
+fp4kv_status fp4kv_swa_ring_append(const void* k_src, const void* v_src, int64_t n_rows, int32_t C,
+                                   const int32_t* row_seq, const int64_t* row_pos, int32_t n_seq,
+                                   int32_t W, void* ring_k, void* ring_v, void* stream);
+
+/*
+ * fp4kv_index_full over a paged indexer-key store idx_k [n_pages*page_rows, D]:
+ * query i belongs to sequence i / q_per_seq (n_q <= n_seq * q_per_seq); every
+ * other argument and every output as for fp4kv_index_full, with
+ * max_ctx <= max_pages*page_rows. Queries are scanned one by one (the
+ * matrix-core scan for many queries per sequence needs contiguous keys).
+ */
+fp4kv_status fp4kv_index_full_paged(const void* idx_q, const float* w, const void* idx_k,
+                                    const int32_t* block_table, int32_t n_seq, int32_t max_pages,
+                                    int32_t page_rows, int64_t n_pages, const int32_t* q_pos,
+                                    int32_t n_q, int32_t q_per_seq, int32_t H, int32_t D,
+                                    int64_t max_ctx, int32_t block, int32_t P, int32_t k,
+                                    int32_t* pool_out, int32_t* n_pool, int32_t* idx_out,
+                                    int32_t* n_idx, void* workspace, size_t ws_bytes, void* stream);
+
+/* fp4kv_index_reindex over a paged indexer-key store (arguments as above). */
+fp4kv_status fp4kv_index_reindex_paged(const void* idx_q, const float* w, const void* idx_k,
+                                       const int32_t* block_table, int32_t n_seq, int32_t max_pages,
+                                       int32_t page_rows, int64_t n_pages, const int32_t* q_pos,
+                                       int32_t n_q, int32_t q_per_seq, int32_t H, int32_t D,
+                                       const int32_t* pool, const int32_t* n_pool, int32_t block,
+                                       int32_t P, int32_t k, int32_t* idx_out, int32_t* n_idx,
+                                       void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * fp4kv_sparse_attn_decode_kv over a paged main-KV store (codes, scales with
+ * n_pages*page_rows rows, one sequence per query: B = n_seq, block_table
+ * [B, max_pages]) and the layer's window ring (ring_k, ring_v [B, W, C]): the
+ * window of query b at position p is positions max(0, p-W+1)..p, read from
+ * slots t mod W. Every other argument as for fp4kv_sparse_attn_decode_kv.
+ */
+fp4kv_status fp4kv_sparse_attn_decode_paged(int32_t fmt, const void* q, const uint8_t* codes,
+                                            const uint8_t* scales, const int32_t* block_table,
+                                            int32_t max_pages, int32_t page_rows, int64_t n_pages,
+                                            const int32_t* idx, const int32_t* n_idx,
+                                            const void* ring_k, const void* ring_v,
+                                            const int32_t* q_pos, int32_t B, int32_t Hq, int32_t C,
+                                            int32_t k, int32_t W, float scale, float* out, float* lse,
+                                            void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

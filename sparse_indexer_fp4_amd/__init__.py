@@ -52,6 +52,15 @@ _SIGS = {
                                            _i32, _f32, _p, _p, _p, _sz, _p]),
     "fp4kv_sparse_attn_prefill_kv": (_i32, [_i32, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f32, _p, _p, _p, _sz, _p]),
+    "fp4kv_paged_kv_append": (_i32, [_i32, _p, _p, _i64, _i32, _i32, _p, _p, _p, _i32, _i32, _i32, _i64, _p, _p, _p,
+                                     _p]),
+    "fp4kv_swa_ring_append": (_i32, [_p, _p, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p]),
+    "fp4kv_index_full_paged": (_i32, [_p, _p, _p, _p, _i32, _i32, _i32, _i64, _p, _i32, _i32, _i32, _i32, _i64, _i32,
+                                      _i32, _i32, _p, _p, _p, _p, _p, _sz, _p]),
+    "fp4kv_index_reindex_paged": (_i32, [_p, _p, _p, _p, _i32, _i32, _i32, _i64, _p, _i32, _i32, _i32, _i32, _p, _p,
+                                         _i32, _i32, _i32, _p, _p, _p, _sz, _p]),
+    "fp4kv_sparse_attn_decode_paged": (_i32, [_i32, _p, _p, _p, _p, _i32, _i32, _i64, _p, _p, _p, _p, _p, _i32, _i32,
+                                              _i32, _i32, _i32, _f32, _p, _p, _p, _sz, _p]),
 }
 
 # Main-KV formats (FP4KV_KV_* in the header).
@@ -289,4 +298,94 @@ def fp4kv_sparse_attn_prefill_kv(fmt, q, codes, scales, seq_start, idx, n_idx, s
                                             _ptr(idx), _ptr(n_idx), _ptr(swa_k), _ptr(swa_v), int(pos0), T, Hq, C, k,
                                             W, float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
                                             _stream(stream)))
+    return out, lse
+
+
+class PagedCache:
+    """Device tensors of a paged cache: block_table int32 [n_seq, max_pages],
+    codes/scales of n_pages*page_rows rows in format fmt, indexer keys idx_k
+    [n_pages*page_rows, D] bf16. A plain holder; nothing is computed here."""
+
+    def __init__(self, block_table, page_rows, n_pages, codes, scales, idx_k, fmt=KV_FP4):
+        self.block_table, self.page_rows, self.n_pages = block_table, int(page_rows), int(n_pages)
+        self.codes, self.scales, self.idx_k, self.fmt = codes, scales, idx_k, fmt
+
+    @property
+    def n_seq(self):
+        return self.block_table.shape[0]
+
+    @property
+    def max_pages(self):
+        return self.block_table.shape[1]
+
+
+def fp4kv_paged_kv_append(cache, row_seq, row_pos, kv_src=None, idxk_src=None, stream=None):
+    """Append rows (main KV and/or indexer keys) at (row_seq[i], row_pos[i]) of a PagedCache."""
+    _expect(row_seq, torch.int32, "row_seq"); _expect(row_pos, torch.int64, "row_pos")
+    n = (kv_src if kv_src is not None else idxk_src).shape[0]
+    C = kv_src.shape[1] if kv_src is not None else 0
+    D = idxk_src.shape[1] if idxk_src is not None else 0
+    _check(lib.fp4kv_paged_kv_append(cache.fmt, _ptr(kv_src), _ptr(idxk_src), n, C, D, _ptr(row_seq), _ptr(row_pos),
+                                     _ptr(cache.block_table), cache.n_seq, cache.max_pages, cache.page_rows,
+                                     cache.n_pages, _ptr(cache.codes), _ptr(cache.scales), _ptr(cache.idx_k),
+                                     _stream(stream)))
+
+
+def fp4kv_swa_ring_append(k_src, v_src, row_seq, row_pos, ring_k, ring_v, stream=None):
+    """Write window rows to slot row_pos mod W of each row's sequence in a ring [n_seq, W, C]."""
+    _expect(k_src, torch.bfloat16, "k_src"); _expect(v_src, torch.bfloat16, "v_src")
+    n, C = k_src.shape
+    n_seq, W, _ = ring_k.shape
+    _check(lib.fp4kv_swa_ring_append(_ptr(k_src), _ptr(v_src), n, C, _ptr(row_seq), _ptr(row_pos), n_seq, W,
+                                     _ptr(ring_k), _ptr(ring_v), _stream(stream)))
+
+
+def fp4kv_index_full_paged(idx_q, w, cache, q_pos, q_per_seq, max_ctx, P, k, block=8, workspace=None, stream=None):
+    """Full-layer indexer over the paged keys of a PagedCache. Returns (pool, n_pool, idx, n_idx)."""
+    n_q, H, D = idx_q.shape
+    dev = idx_q.device
+    pool = torch.empty((n_q, P), dtype=torch.int32, device=dev)
+    n_pool = torch.empty((n_q,), dtype=torch.int32, device=dev)
+    idx = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    n_idx = torch.empty((n_q,), dtype=torch.int32, device=dev)
+    ws = _workspace(fp4kv_index_workspace_bytes(n_q, max_ctx, block), dev, workspace)
+    _check(lib.fp4kv_index_full_paged(_ptr(idx_q), _ptr(w), _ptr(cache.idx_k), _ptr(cache.block_table), cache.n_seq,
+                                      cache.max_pages, cache.page_rows, cache.n_pages, _ptr(q_pos), n_q, q_per_seq, H,
+                                      D, max_ctx, block, P, k, _ptr(pool), _ptr(n_pool), _ptr(idx), _ptr(n_idx),
+                                      _ptr(ws), ws.numel(), _stream(stream)))
+    return pool, n_pool, idx, n_idx
+
+
+def fp4kv_index_reindex_paged(idx_q, w, cache, q_pos, q_per_seq, pool, n_pool, k, block=8, workspace=None,
+                              stream=None):
+    """Reindex over the paged keys of a PagedCache with an inherited pool. Returns (idx, n_idx)."""
+    n_q, H, D = idx_q.shape
+    P = pool.shape[1]
+    dev = idx_q.device
+    idx = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    n_idx = torch.empty((n_q,), dtype=torch.int32, device=dev)
+    ws = _workspace(fp4kv_reindex_workspace_bytes(n_q, P, block), dev, workspace)
+    _check(lib.fp4kv_index_reindex_paged(_ptr(idx_q), _ptr(w), _ptr(cache.idx_k), _ptr(cache.block_table),
+                                         cache.n_seq, cache.max_pages, cache.page_rows, cache.n_pages, _ptr(q_pos),
+                                         n_q, q_per_seq, H, D, _ptr(pool), _ptr(n_pool), block, P, k, _ptr(idx),
+                                         _ptr(n_idx), _ptr(ws), ws.numel(), _stream(stream)))
+    return idx, n_idx
+
+
+def fp4kv_sparse_attn_decode_paged(q, cache, idx, n_idx, ring_k, ring_v, q_pos, scale, out=None, lse=None,
+                                   workspace=None, stream=None):
+    """Decode attention over the paged main KV of a PagedCache and a window ring [B, W, C]."""
+    _expect(q, torch.bfloat16, "q"); _expect(idx, torch.int32, "idx"); _expect(n_idx, torch.int32, "n_idx")
+    B, Hq, C = q.shape
+    k = idx.shape[1]
+    W = ring_k.shape[1]
+    dev = q.device
+    out = torch.empty((B, Hq, C), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    ws = _workspace(fp4kv_attn_workspace_bytes(B, Hq, C, k, W), dev, workspace)
+    _check(lib.fp4kv_sparse_attn_decode_paged(cache.fmt, _ptr(q), _ptr(cache.codes), _ptr(cache.scales),
+                                              _ptr(cache.block_table), cache.max_pages, cache.page_rows,
+                                              cache.n_pages, _ptr(idx), _ptr(n_idx), _ptr(ring_k), _ptr(ring_v),
+                                              _ptr(q_pos), B, Hq, C, k, W, float(scale), _ptr(out), _ptr(lse),
+                                              _ptr(ws), ws.numel(), _stream(stream)))
     return out, lse

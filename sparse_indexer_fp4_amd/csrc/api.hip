@@ -75,7 +75,10 @@ fp4kv_status fp4kv_kv_append(int32_t fmt, const void* src, int64_t n_rows, int32
   if (!aligned16(src) || (reinterpret_cast<uintptr_t>(codes) & 7u))
     return fail(FP4KV_ERR_SHAPE, "kv_append: src must be 16-byte and codes 8-byte aligned");
   if (n_rows == 0) return ok();
-  return hip_status(fp4kv::launch_quantize_append(fmt, src, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows,
+  fp4kv::AppendDst dd{};
+  dd.dst_rows = dst_rows;
+  dd.dst_start = dst_start;
+  return hip_status(fp4kv::launch_quantize_append(fmt, src, n_rows, C, dd, codes, scales, cap_rows,
                                                   static_cast<hipStream_t>(stream)),
                     "kv_append");
 }
@@ -122,8 +125,9 @@ static fp4kv_status check_indexer_common(const char* fn, const void* idx_q, cons
 static fp4kv_status launch_scores(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
                                   const int64_t* seq_start, const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
                                   int32_t H, int32_t D, int64_t max_ctx, int32_t block, float* scores,
-                                  float* blockmax, hipStream_t s) {
+                                  float* blockmax, hipStream_t s, const fp4kv::PageMap* map = nullptr) {
   fp4kv::ScanArgs sa{};
+  if (map) sa.map = *map;
   sa.idx_q = static_cast<const uint16_t*>(idx_q);
   sa.w = w;
   sa.idx_k = static_cast<const uint16_t*>(idx_k);
@@ -135,8 +139,9 @@ static fp4kv_status launch_scores(const void* idx_q, const float* w, const void*
   sa.scores = scores;
   sa.blockmax = blockmax;
   sa.nblk_max = nblk_of(max_ctx, block);
-  // Many queries per sequence share every key: the scan is a dense product on the matrix cores.
-  if (fp4kv::scan_mfma_supported(H, D, q_per_seq) && max_ctx <= INT32_MAX)
+  // Many queries per sequence share every key: the scan is a dense product on the matrix cores
+  // (contiguous storage only; a paged cache is scanned query by query).
+  if (!map && fp4kv::scan_mfma_supported(H, D, q_per_seq) && max_ctx <= INT32_MAX)
     return hip_status(fp4kv::launch_scan_mfma(sa, H, D, n_q, s), "index scan (matrix cores)");
   return hip_status(fp4kv::launch_scan(sa, H, D, n_q, max_ctx, false, s), "index scan");
 }
@@ -379,6 +384,202 @@ fp4kv_status fp4kv_sparse_attn_prefill(const void* q, const uint8_t* codes, cons
                                        size_t ws_bytes, void* stream) {
   return fp4kv_sparse_attn_prefill_kv(FP4KV_KV_FP4, q, codes, scales, total_rows, seq_start, idx, n_idx, swa_k,
                                       swa_v, pos0, T, Hq, C, k, W, scale, out, lse, workspace, ws_bytes, stream);
+}
+
+// ---- paged cache and window ring ------------------------------------------
+
+static fp4kv_status check_pages(const char* fn, const int32_t* block_table, int32_t n_seq, int32_t max_pages,
+                                int32_t page_rows, int64_t n_pages, fp4kv::PageMap& m) {
+  if (!block_table) return fail(FP4KV_ERR_NULL, "%s: block_table must be non-NULL", fn);
+  if (n_seq < 0 || max_pages < 1 || n_pages < 1)
+    return fail(FP4KV_ERR_SHAPE, "%s: n_seq >= 0, max_pages >= 1 and n_pages >= 1 required", fn);
+  if (page_rows < 64 || page_rows > (1 << 20) || (page_rows & (page_rows - 1)) != 0)
+    return fail(FP4KV_ERR_SHAPE, "%s: page_rows=%d must be a power of two in [64, 2^20]", fn, page_rows);
+  if (n_pages > (INT64_MAX >> 21)) return fail(FP4KV_ERR_SHAPE, "%s: n_pages too large", fn);
+  m.block_table = block_table;
+  m.n_seq = n_seq;
+  m.max_pages = max_pages;
+  m.log2_page = __builtin_ctz((unsigned)page_rows);
+  m.n_pages = n_pages;
+  return FP4KV_OK;
+}
+
+fp4kv_status fp4kv_paged_kv_append(int32_t fmt, const void* kv_src, const void* idxk_src, int64_t n_rows, int32_t C,
+                                   int32_t D, const int32_t* row_seq, const int64_t* row_pos,
+                                   const int32_t* block_table, int32_t n_seq, int32_t max_pages, int32_t page_rows,
+                                   int64_t n_pages, uint8_t* codes, uint8_t* scales, void* idx_k, void* stream) {
+  const char* fn = "paged_kv_append";
+  if (!valid_fmt(fmt)) return fail(FP4KV_ERR_UNSUPPORTED, "%s: format %d (0, 1 or 2 implemented)", fn, fmt);
+  fp4kv::AppendDst dd{};
+  fp4kv_status st = check_pages(fn, block_table, n_seq, max_pages, page_rows, n_pages, dd.map);
+  if (st != FP4KV_OK) return st;
+  if (!row_seq || !row_pos || (!kv_src && !idxk_src))
+    return fail(FP4KV_ERR_NULL, "%s: row_seq, row_pos and one of kv_src / idxk_src must be non-NULL", fn);
+  if (kv_src && (!codes || (fmt != FP4KV_KV_FP8 && !scales)))
+    return fail(FP4KV_ERR_NULL, "%s: codes and (except for FP8) scales must be non-NULL with kv_src", fn);
+  if (idxk_src && !idx_k) return fail(FP4KV_ERR_NULL, "%s: idx_k must be non-NULL with idxk_src", fn);
+  if (n_rows < 0) return fail(FP4KV_ERR_SHAPE, "%s: n_rows must be >= 0", fn);
+  if (kv_src && (C <= 0 || C % 32 != 0)) return fail(FP4KV_ERR_SHAPE, "%s: C=%d must be a positive multiple of 32", fn, C);
+  if (idxk_src && (D <= 0 || D % 8 != 0)) return fail(FP4KV_ERR_SHAPE, "%s: D=%d must be a positive multiple of 8", fn, D);
+  if ((kv_src && !aligned16(kv_src)) || (idxk_src && (!aligned16(idxk_src) || !aligned16(idx_k))) ||
+      (codes && (reinterpret_cast<uintptr_t>(codes) & 7u)))
+    return fail(FP4KV_ERR_SHAPE, "%s: kv_src, idxk_src, idx_k must be 16-byte and codes 8-byte aligned", fn);
+  if (n_rows == 0) return ok();
+  dd.row_seq = row_seq;
+  dd.row_pos = row_pos;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t cap = n_pages << dd.map.log2_page;
+  if (kv_src) {
+    st = hip_status(fp4kv::launch_quantize_append(fmt, kv_src, n_rows, C, dd, codes, scales, cap, s), fn);
+    if (st != FP4KV_OK) return st;
+  }
+  if (idxk_src) return hip_status(fp4kv::launch_copy_rows(idxk_src, n_rows, D, dd, idx_k, cap, s), fn);
+  return ok();
+}
+
+fp4kv_status fp4kv_swa_ring_append(const void* k_src, const void* v_src, int64_t n_rows, int32_t C,
+                                   const int32_t* row_seq, const int64_t* row_pos, int32_t n_seq, int32_t W,
+                                   void* ring_k, void* ring_v, void* stream) {
+  const char* fn = "swa_ring_append";
+  if (!k_src || !v_src || !row_seq || !row_pos || !ring_k || !ring_v)
+    return fail(FP4KV_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (n_rows < 0 || n_seq < 0 || W < 1 || C <= 0 || C % 8 != 0)
+    return fail(FP4KV_ERR_SHAPE, "%s: n_rows=%lld n_seq=%d W=%d C=%d out of range", fn, (long long)n_rows, n_seq, W, C);
+  if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(ring_k) || !aligned16(ring_v))
+    return fail(FP4KV_ERR_SHAPE, "%s: all row buffers must be 16-byte aligned", fn);
+  if (n_rows == 0) return ok();
+  return hip_status(fp4kv::launch_ring_append(k_src, v_src, n_rows, C, row_seq, row_pos, n_seq, W, ring_k, ring_v,
+                                              static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+fp4kv_status fp4kv_index_full_paged(const void* idx_q, const float* w, const void* idx_k, const int32_t* block_table,
+                                    int32_t n_seq, int32_t max_pages, int32_t page_rows, int64_t n_pages,
+                                    const int32_t* q_pos, int32_t n_q, int32_t q_per_seq, int32_t H, int32_t D,
+                                    int64_t max_ctx, int32_t block, int32_t P, int32_t k, int32_t* pool_out,
+                                    int32_t* n_pool, int32_t* idx_out, int32_t* n_idx, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+  const char* fn = "index_full_paged";
+  fp4kv::PageMap m{};
+  fp4kv_status st = check_pages(fn, block_table, n_seq, max_pages, page_rows, n_pages, m);
+  if (st != FP4KV_OK) return st;
+  const int64_t total_rows = n_pages * page_rows;
+  const int64_t dummy_start = 0;     // not read: the block table places every row
+  st = check_indexer_common(fn, idx_q, w, idx_k, total_rows, &dummy_start, q_pos, n_q, q_per_seq, H, D, block, P, k,
+                            idx_out, n_idx);
+  if (st != FP4KV_OK) return st;
+  if (!pool_out || !n_pool) return fail(FP4KV_ERR_NULL, "%s: pool_out and n_pool must be non-NULL", fn);
+  if (max_ctx < 1 || max_ctx > (int64_t)max_pages * page_rows)
+    return fail(FP4KV_ERR_SHAPE, "%s: max_ctx=%lld must be in [1, max_pages*page_rows]", fn, (long long)max_ctx);
+  if ((int64_t)n_q > (int64_t)n_seq * q_per_seq)
+    return fail(FP4KV_ERR_SHAPE, "%s: n_q=%d exceeds n_seq*q_per_seq", fn, n_q);
+  if (n_q == 0) return ok();
+  const size_t need = fp4kv_index_workspace_bytes(n_q, max_ctx, block);
+  if (!workspace || ws_bytes < need)
+    return fail(FP4KV_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu required", fn, ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* scores = static_cast<float*>(workspace);
+  float* blockmax = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)n_q * max_ctx * sizeof(float)));
+  st = launch_scores(idx_q, w, idx_k, total_rows, nullptr, q_pos, n_q, q_per_seq, H, D, max_ctx, block, scores,
+                     blockmax, s, &m);
+  if (st != FP4KV_OK) return st;
+  return launch_select_full(scores, blockmax, INT64_MAX, nullptr, q_pos, n_q, q_per_seq, max_ctx, block, P, k,
+                            pool_out, n_pool, idx_out, n_idx, s);
+}
+
+fp4kv_status fp4kv_index_reindex_paged(const void* idx_q, const float* w, const void* idx_k,
+                                       const int32_t* block_table, int32_t n_seq, int32_t max_pages,
+                                       int32_t page_rows, int64_t n_pages, const int32_t* q_pos, int32_t n_q,
+                                       int32_t q_per_seq, int32_t H, int32_t D, const int32_t* pool,
+                                       const int32_t* n_pool, int32_t block, int32_t P, int32_t k, int32_t* idx_out,
+                                       int32_t* n_idx, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "index_reindex_paged";
+  fp4kv::PageMap m{};
+  fp4kv_status st = check_pages(fn, block_table, n_seq, max_pages, page_rows, n_pages, m);
+  if (st != FP4KV_OK) return st;
+  const int64_t total_rows = n_pages * page_rows;
+  const int64_t dummy_start = 0;
+  st = check_indexer_common(fn, idx_q, w, idx_k, total_rows, &dummy_start, q_pos, n_q, q_per_seq, H, D, block, P, k,
+                            idx_out, n_idx);
+  if (st != FP4KV_OK) return st;
+  if (!pool || !n_pool) return fail(FP4KV_ERR_NULL, "%s: pool and n_pool must be non-NULL", fn);
+  if ((int64_t)n_q > (int64_t)n_seq * q_per_seq)
+    return fail(FP4KV_ERR_SHAPE, "%s: n_q=%d exceeds n_seq*q_per_seq", fn, n_q);
+  if (n_q == 0) return ok();
+  const size_t need = fp4kv_reindex_workspace_bytes(n_q, P, block);
+  if (!workspace || ws_bytes < need)
+    return fail(FP4KV_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu required", fn, ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  fp4kv::ScanArgs sa{};
+  sa.idx_q = static_cast<const uint16_t*>(idx_q);
+  sa.w = w;
+  sa.idx_k = static_cast<const uint16_t*>(idx_k);
+  sa.total_rows = total_rows;
+  sa.seq_start = nullptr;
+  sa.q_pos = q_pos;
+  sa.q_per_seq = q_per_seq;
+  sa.max_ctx = (int64_t)max_pages * page_rows;   // every position the table can map
+  sa.pool = pool;
+  sa.n_pool = n_pool;
+  sa.P = P;
+  sa.pool_scores = static_cast<float*>(workspace);
+  sa.map = m;
+  hipError_t e = fp4kv::launch_scan(sa, H, D, n_q, (int64_t)P * block, true, s);
+  if (e != hipSuccess) return hip_status(e, "index_reindex_paged scan");
+  fp4kv::SelectArgs se{};
+  se.seq_start = nullptr;
+  se.q_pos = q_pos;
+  se.q_per_seq = q_per_seq;
+  se.total_rows = INT64_MAX;
+  se.max_ctx = (int64_t)max_pages * page_rows;
+  se.scores = static_cast<float*>(workspace);
+  se.P = P;
+  se.k = k;
+  se.pool = const_cast<int32_t*>(pool);
+  se.n_pool = const_cast<int32_t*>(n_pool);
+  se.idx_out = idx_out;
+  se.n_idx = n_idx;
+  return hip_status(fp4kv::launch_select(se, n_q, true, s), "index_reindex_paged select");
+}
+
+fp4kv_status fp4kv_sparse_attn_decode_paged(int32_t fmt, const void* q, const uint8_t* codes, const uint8_t* scales,
+                                            const int32_t* block_table, int32_t max_pages, int32_t page_rows,
+                                            int64_t n_pages, const int32_t* idx, const int32_t* n_idx,
+                                            const void* ring_k, const void* ring_v, const int32_t* q_pos, int32_t B,
+                                            int32_t Hq, int32_t C, int32_t k, int32_t W, float scale, float* out,
+                                            float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "sparse_attn_decode_paged";
+  fp4kv::PageMap m{};
+  fp4kv_status st = check_pages(fn, block_table, B, max_pages, page_rows, n_pages, m);
+  if (st != FP4KV_OK) return st;
+  st = check_attn(fn, fmt, q, codes, scales, idx, n_idx, ring_k, ring_v, B, Hq, C, k, W, scale, out, workspace,
+                  ws_bytes);
+  if (st != FP4KV_OK) return st;
+  if (!q_pos) return fail(FP4KV_ERR_NULL, "%s: q_pos must be non-NULL", fn);
+  if (B == 0) return ok();
+  fp4kv::AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.codes = codes;
+  a.scales = fmt == FP4KV_KV_FP8 ? nullptr : scales;
+  a.kv_fmt = fmt;
+  a.total_rows = n_pages * page_rows;
+  a.idx = idx;
+  a.n_idx = n_idx;
+  a.k = k;
+  a.swa_k = static_cast<const uint16_t*>(ring_k);
+  a.swa_v = static_cast<const uint16_t*>(ring_v);
+  a.q_pos = q_pos;
+  a.win_stride = W;
+  a.W = W;
+  a.nq = B;
+  a.Hq = Hq;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  a.map = m;
+  a.page_q_per_seq = 1;
+  a.ring = 1;
+  return hip_status(fp4kv::launch_attn(a, workspace, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

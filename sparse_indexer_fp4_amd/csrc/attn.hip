@@ -101,16 +101,19 @@ struct RawWindow {
 };
 
 struct QueryInfo {
-  int64_t kv_base;    // first main-KV row of the sequence
+  int64_t kv_base;    // first main-KV row of the sequence (contiguous storage)
+  int64_t seq;        // sequence of the query (paged storage)
   int64_t p;          // query position
   int n_s, n_w;       // sparse rows, window rows
   int cs, cw;         // chunks of each
   int64_t win_row0;   // window-buffer row holding the oldest used window row
+  int64_t ring_base;  // window ring: first row of the query's W rows
 };
 
 __device__ __forceinline__ QueryInfo query_info(const AttnArgs& a, int qi) {
   QueryInfo r;
-  r.kv_base = a.seq_start ? a.seq_start[qi] : a.seq_start_scalar;
+  r.kv_base = a.map.block_table ? 0 : (a.seq_start ? a.seq_start[qi] : a.seq_start_scalar);
+  r.seq = a.map.block_table ? qi / a.page_q_per_seq : 0;
   int64_t p = a.q_pos ? (int64_t)a.q_pos[qi] : (int64_t)a.pos0 + qi;
   r.p = p;            // negative: the query sees no token
   int ns = a.n_idx[qi];
@@ -119,14 +122,15 @@ __device__ __forceinline__ QueryInfo query_info(const AttnArgs& a, int qi) {
   r.cs = (r.n_s + kChunk - 1) / kChunk;
   r.cw = (r.n_w + kChunk - 1) / kChunk;
   r.win_row0 = (int64_t)qi * a.win_stride + (a.W - r.n_w);
+  r.ring_base = (int64_t)qi * a.W;
   return r;
 }
 
-// Main-KV row of sparse slot j holding position `pos`, or -1 if the slot is
-// not a usable row.
-__device__ __forceinline__ int64_t sparse_row(const AttnArgs& a, const QueryInfo& qi_, int j, int64_t pos) {
-  if (j >= qi_.n_s || pos < 0 || pos > qi_.p) return -1;
-  int64_t row = qi_.kv_base + pos;
+// Main-KV row of sparse slot j holding position `pos` at storage row `row`
+// (already mapped), or -1 if the slot is not a usable row.
+__device__ __forceinline__ int64_t sparse_row(const AttnArgs& a, const QueryInfo& qi_, int j, int64_t pos,
+                                              int64_t row) {
+  if (j >= qi_.n_s || pos < 0 || pos > qi_.p || row < 0) return -1;
   return row < a.total_rows ? row : -1;
 }
 
@@ -137,31 +141,59 @@ __device__ __forceinline__ int item_rows(int item) { return __builtin_amdgcn_rea
 // The selected positions a wave needs are read with one vector load when the
 // workgroup starts: lane l holds the position of row 4*rg + (l & 3) of the
 // m-th chunk of this split, where m = l / (4 PER) and rg is the row group of the
-// wave's item (l / 4) % PER. Chunks past the 16/PER covered read their
-// positions directly.
-template <int NHG>
-__device__ __forceinline__ int idx_lane_load(const AttnArgs& a, int qi, int split, int lane) {
+// wave's item (l / 4) % PER. With paged storage the lane also maps it through
+// the block table (one more vector load) and holds the physical row. Chunks
+// past the 16/PER covered read and map their positions directly.
+struct LanePos {
+  int pos;
+  uint32_t row_lo, row_hi;     // paged: physical row
+};
+
+template <int NHG, bool PAGED>
+__device__ __forceinline__ LanePos idx_lane_load(const AttnArgs& a, int qi, int split, int lane) {
   constexpr int PER = kItems / (128 * NHG);
   const int m = lane / (4 * PER), it = (lane / 4) % PER, r = lane & 3;
   const int rg = (int)(threadIdx.x >> 6) + it * 2 * NHG;   // item_rows of item threadIdx.x + it * 128 * NHG
   const int j = (split + m * a.n_split) * kChunk + 4 * rg + r;
-  return j < a.k ? a.idx[(int64_t)qi * a.k + j] : -1;
+  LanePos lp;
+  lp.pos = j < a.k ? a.idx[(int64_t)qi * a.k + j] : -1;
+  lp.row_lo = lp.row_hi = 0;
+  if constexpr (PAGED) {
+    const int64_t row = paged_row(a.map, qi / a.page_q_per_seq, lp.pos);
+    lp.row_lo = (uint32_t)row;
+    lp.row_hi = (uint32_t)((uint64_t)row >> 32);
+  }
+  return lp;
 }
 
-template <int NHG>
-__device__ __forceinline__ int64_t chunk_pos(const AttnArgs& a, int qi, int m, int j, int it, int r, int idxv) {
+// Storage row of sparse slot j (the m-th chunk of the split, item it, row r),
+// or -1 if the slot is not a usable row.
+template <int NHG, bool PAGED>
+__device__ __forceinline__ int64_t chunk_row(const AttnArgs& a, const QueryInfo& Q, int qi, int m, int j, int it,
+                                             int r, const LanePos& lp) {
   constexpr int PER = kItems / (128 * NHG);
-  if (m < 16 / PER) return __builtin_amdgcn_readlane(idxv, (m * PER + it) * 4 + r);
-  return j < a.k ? a.idx[(int64_t)qi * a.k + j] : -1;
+  int64_t pos, row;
+  if (m < 16 / PER) {
+    const int l = (m * PER + it) * 4 + r;
+    pos = __builtin_amdgcn_readlane(lp.pos, l);
+    if constexpr (PAGED)
+      row = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lp.row_hi, l) << 32) |
+                      (uint32_t)__builtin_amdgcn_readlane((int)lp.row_lo, l));
+  } else {
+    pos = j < a.k ? a.idx[(int64_t)qi * a.k + j] : -1;
+    if constexpr (PAGED) row = paged_row(a.map, Q.seq, pos);
+  }
+  if constexpr (!PAGED) row = Q.kv_base + pos;
+  return sparse_row(a, Q, j, pos, row);
 }
 
 // Issue the loads of chunk c, the m-th chunk of this split: FP4 codes and
 // scales of a sparse chunk, or bf16 keys and values of a window chunk. The
 // registers are not read until the chunk is committed, so the loads stay in
 // flight while the current chunk is computed.
-template <int NHG, int FMT>
-__device__ __forceinline__ void load_sparse(const AttnArgs& a, const QueryInfo& Q, int qi, int c, int m, int idxv,
-                                            RawSparse (&raw)[kItems / (128 * NHG)]) {
+template <int NHG, int FMT, bool PAGED>
+__device__ __forceinline__ void load_sparse(const AttnArgs& a, const QueryInfo& Q, int qi, int c, int m,
+                                            const LanePos& lp, RawSparse (&raw)[kItems / (128 * NHG)]) {
   constexpr int PER = kItems / (128 * NHG);
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
@@ -171,7 +203,7 @@ __device__ __forceinline__ void load_sparse(const AttnArgs& a, const QueryInfo& 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = c * kChunk + 4 * rg + r;
-      const int64_t row = sparse_row(a, Q, j, chunk_pos<NHG>(a, qi, m, j, it, r, idxv));
+      const int64_t row = chunk_row<NHG, PAGED>(a, Q, qi, m, j, it, r, lp);
       const int64_t rr = row < 0 ? 0 : row;
       if constexpr (FMT == kKvFp8) {
         const uint2 v = *reinterpret_cast<const uint2*>(a.codes + rr * kAttnC + 8 * cg);
@@ -203,7 +235,9 @@ __device__ __forceinline__ void load_window(const AttnArgs& a, const QueryInfo& 
       const int wr = (c - Q.cs) * kChunk + 4 * rg + r;
       const bool ok = wr < Q.n_w;
       bits |= (uint32_t)ok << r;
-      const int64_t row = Q.win_row0 + (ok ? wr : 0);
+      // a ring keeps position t in slot t mod W of the query's W rows
+      const int64_t row = a.ring ? Q.ring_base + (Q.p - Q.n_w + 1 + (ok ? wr : 0)) % a.W
+                                 : Q.win_row0 + (ok ? wr : 0);
       raw[it].k[r] = *reinterpret_cast<const uint4*>(a.swa_k + row * kAttnC + 8 * cg);
       raw[it].v[r] = *reinterpret_cast<const uint4*>(a.swa_v + row * kAttnC + 8 * cg);
     }
@@ -308,7 +342,7 @@ __device__ __forceinline__ void commit_window(AttnShared<NHG>& sh, const RawWind
 // of the 512 output channels (64 accumulators per lane, so two waves fit on a
 // SIMD). The two waves of a head group each form S over their half of the
 // channels and exchange the partial sums through LDS.
-template <int NHG, int FMT>
+template <int NHG, int FMT, bool PAGED>
 __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   constexpr int PER = kItems / (128 * NHG);
   __shared__ AttnShared<NHG> sh;
@@ -317,7 +351,7 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   const int hg = wave >> 1, hc = wave & 1;          // head group, channel half
   const int g = lane / 16, hcol = lane % 16;
   const int head = hg * 16 + hcol;
-  const int idxv = idx_lane_load<NHG>(a, qi, split, lane);
+  const LanePos lp = idx_lane_load<NHG, PAGED>(a, qi, split, lane);
   const QueryInfo Q = query_info(a, qi);
   const int nchunk = Q.cs + Q.cw;
 
@@ -343,7 +377,7 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   const int nW = nT - nS, w0 = nW > 0 ? 1 : 0;
   RawSparse rs[PER];
   RawWindow rw[PER];
-  if (nS > 0) load_sparse<NHG, FMT>(a, Q, qi, split, 0, idxv, rs);
+  if (nS > 0) load_sparse<NHG, FMT, PAGED>(a, Q, qi, split, 0, lp, rs);
   // (with several items per thread the window slot would not fit in registers
   // beside the accumulators: the first window chunk is then loaded at commit)
   if constexpr (PER == 1) {
@@ -387,7 +421,7 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
       commit_window<NHG>(sh, tw);
     }
     __syncthreads();
-    if (step >= w0 && i + 1 < nS) load_sparse<NHG, FMT>(a, Q, qi, split + (i + 1) * ns_, i + 1, idxv, rs);
+    if (step >= w0 && i + 1 < nS) load_sparse<NHG, FMT, PAGED>(a, Q, qi, split + (i + 1) * ns_, i + 1, lp, rs);
 
     // partial S^T over this channel half: A = even rows (tile 0) / odd rows (tile 1), B = Q^T
     v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -545,8 +579,12 @@ hipError_t launch_attn(AttnArgs a, void* ws, hipStream_t stream) {
   const int nhg = a.Hq / 16;
   dim3 grid((uint32_t)a.n_split, (uint32_t)a.nq);
   if (a.kv_fmt < kKvFp4 || a.kv_fmt > kKvFp8) return hipErrorInvalidValue;
-#define FP4KV_ATTN_CASE(NH, FM) \
-  if (nhg == NH && a.kv_fmt == FM) attn_kernel<NH, FM><<<grid, dim3(128 * NH), 0, stream>>>(a); else
+  const bool paged = a.map.block_table != nullptr;
+#define FP4KV_ATTN_CASE(NH, FM)                                                                  \
+  if (nhg == NH && a.kv_fmt == FM) {                                                             \
+    if (paged) attn_kernel<NH, FM, true><<<grid, dim3(128 * NH), 0, stream>>>(a);                 \
+    else attn_kernel<NH, FM, false><<<grid, dim3(128 * NH), 0, stream>>>(a);                      \
+  } else
   FP4KV_ATTN_CASE(1, kKvFp4) FP4KV_ATTN_CASE(2, kKvFp4) FP4KV_ATTN_CASE(4, kKvFp4)
   FP4KV_ATTN_CASE(1, kKvMxfp4) FP4KV_ATTN_CASE(2, kKvMxfp4) FP4KV_ATTN_CASE(4, kKvMxfp4)
   FP4KV_ATTN_CASE(1, kKvFp8) FP4KV_ATTN_CASE(2, kKvFp8) FP4KV_ATTN_CASE(4, kKvFp8)

@@ -12,6 +12,42 @@ enum KvFmt : int32_t {
   kKvFp8 = 2,     // one E4M3FN code per channel, no scale
 };
 
+// Paged storage: a sequence's positions in pages of 2^log2_page rows;
+// block_table[s * max_pages + i] is the physical page of sequence s's page i,
+// rows page << log2_page .. of every per-token store. block_table == nullptr:
+// contiguous storage (rows seq_start[s] + position).
+struct PageMap {
+  const int32_t* block_table;
+  int32_t n_seq, max_pages, log2_page;
+  int64_t n_pages;
+};
+
+// Physical row of position pos of sequence seq, or -1 where nothing is mapped
+// (sequence, page or page id out of range).
+__device__ __forceinline__ int64_t paged_row(const PageMap& m, int64_t seq, int64_t pos) {
+  if (seq < 0 || seq >= m.n_seq || pos < 0) return -1;
+  const int64_t page = pos >> m.log2_page;
+  if (page >= m.max_pages) return -1;
+  const int64_t g = m.block_table[seq * m.max_pages + page];
+  if (g < 0 || g >= m.n_pages) return -1;
+  return (g << m.log2_page) + (pos & ((int64_t(1) << m.log2_page) - 1));
+}
+
+// Destination rows of appended rows: dst_rows[i], dst_start + i, or (paged)
+// the physical row of (row_seq[i], row_pos[i]); -1 = not written.
+struct AppendDst {
+  const int64_t* dst_rows;
+  int64_t dst_start;
+  const int32_t* row_seq;
+  const int64_t* row_pos;
+  PageMap map;
+};
+
+__device__ __forceinline__ int64_t append_dst(const AppendDst& d, int64_t i) {
+  if (d.map.block_table) return paged_row(d.map, d.row_seq[i], d.row_pos[i]);
+  return d.dst_rows ? d.dst_rows[i] : d.dst_start + i;
+}
+
 struct ScanArgs {
   const uint16_t* idx_q;     // [n_q, H, D] bf16
   const float* w;            // [n_q, H]
@@ -31,6 +67,7 @@ struct ScanArgs {
   int32_t P;
   float* pool_scores;        // [n_q, P*8]
   int32_t steps;             // 64-token steps per workgroup
+  PageMap map;               // paged idx_k when map.block_table (seq_start unused)
 };
 
 // Launch geometry of the matrix-core scan (host-computed).
@@ -45,7 +82,7 @@ struct MfmaScanGrid {
 };
 
 struct SelectArgs {
-  const int64_t* seq_start;
+  const int64_t* seq_start;  // nullptr for paged storage (positions are bounded by max_ctx only)
   const int32_t* q_pos;
   int32_t q_per_seq;
   int64_t total_rows;
@@ -84,11 +121,20 @@ struct AttnArgs {
   float* lse;                     // [nq, Hq] or nullptr
   float* part_o;                  // [nq, n_split, Hq, C]
   float* part_ml;                 // [nq, n_split, Hq, 2]
+  PageMap map;                    // paged main KV when map.block_table
+  int32_t page_q_per_seq;         // paged: query i belongs to sequence i / page_q_per_seq
+  int32_t ring;                   // window rows in a ring [nq, W, C]: position t in slot t mod W
 };
 
-hipError_t launch_quantize_append(int32_t fmt, const void* src, int64_t n_rows, int32_t C,
-                                  const int64_t* dst_rows, int64_t dst_start, uint8_t* codes, uint8_t* scales,
-                                  int64_t cap_rows, hipStream_t stream);
+hipError_t launch_quantize_append(int32_t fmt, const void* src, int64_t n_rows, int32_t C, const AppendDst& dst,
+                                  uint8_t* codes, uint8_t* scales, int64_t cap_rows, hipStream_t stream);
+// Copy of bf16 rows [n_rows, width] to their destinations (indexer keys of a paged cache).
+hipError_t launch_copy_rows(const void* src, int64_t n_rows, int32_t width, const AppendDst& dst, void* out,
+                            int64_t cap_rows, hipStream_t stream);
+// Window ring append: row i to slot row_pos[i] mod W of sequence row_seq[i].
+hipError_t launch_ring_append(const void* k_src, const void* v_src, int64_t n_rows, int32_t C, const int32_t* row_seq,
+                              const int64_t* row_pos, int32_t n_seq, int32_t W, void* ring_k, void* ring_v,
+                              hipStream_t stream);
 bool scan_supported(int H, int D);
 // slots: max_ctx for a Full scan, P*8 for a Reindex scan.
 hipError_t launch_scan(ScanArgs a, int H, int D, int n_q, int64_t slots, bool reindex, hipStream_t stream);

@@ -66,14 +66,14 @@ __device__ __forceinline__ uint32_t encode_value(float x, float s) {
 }
 
 __global__ __launch_bounds__(256) void quantize_append_kernel(
-    const uint16_t* __restrict__ src, int64_t n_rows, int32_t C, const int64_t* __restrict__ dst_rows,
-    int64_t dst_start, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t cap_rows) {
+    const uint16_t* __restrict__ src, int64_t n_rows, int32_t C, AppendDst dd, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t cap_rows) {
   const int32_t G = C >> 4;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= n_rows * G) return;
   const int64_t row = gid / G;
   const int32_t g = (int32_t)(gid - row * G);
-  const int64_t dst = dst_rows ? dst_rows[row] : dst_start + row;
+  const int64_t dst = append_dst(dd, row);
   if (dst < 0 || dst >= cap_rows) return;
 
   const uint4* p = reinterpret_cast<const uint4*>(src + row * C + g * 16);
@@ -118,14 +118,14 @@ __device__ __forceinline__ int mx_shared_exp(uint32_t amax_bits) {
 }
 
 __global__ __launch_bounds__(256) void quantize_mxfp4_kernel(
-    const uint16_t* __restrict__ src, int64_t n_rows, int32_t C, const int64_t* __restrict__ dst_rows,
-    int64_t dst_start, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t cap_rows) {
+    const uint16_t* __restrict__ src, int64_t n_rows, int32_t C, AppendDst dd, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t cap_rows) {
   const int32_t G = C >> 5;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= n_rows * G) return;
   const int64_t row = gid / G;
   const int32_t g = (int32_t)(gid - row * G);
-  const int64_t dst = dst_rows ? dst_rows[row] : dst_start + row;
+  const int64_t dst = append_dst(dd, row);
   if (dst < 0 || dst >= cap_rows) return;
 
   const uint4* p = reinterpret_cast<const uint4*>(src + row * C + g * 32);
@@ -179,14 +179,14 @@ __device__ __forceinline__ uint32_t encode_e4m3(float x) {
 }
 
 __global__ __launch_bounds__(256) void quantize_fp8_kernel(
-    const uint16_t* __restrict__ src, int64_t n_rows, int32_t C, const int64_t* __restrict__ dst_rows,
-    int64_t dst_start, uint8_t* __restrict__ codes, int64_t cap_rows) {
+    const uint16_t* __restrict__ src, int64_t n_rows, int32_t C, AppendDst dd, uint8_t* __restrict__ codes,
+    int64_t cap_rows) {
   const int32_t G = C >> 4;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= n_rows * G) return;
   const int64_t row = gid / G;
   const int32_t g = (int32_t)(gid - row * G);
-  const int64_t dst = dst_rows ? dst_rows[row] : dst_start + row;
+  const int64_t dst = append_dst(dd, row);
   if (dst < 0 || dst >= cap_rows) return;
   const uint4* p = reinterpret_cast<const uint4*>(src + row * C + g * 16);
   const uint4 v0 = p[0], v1 = p[1];
@@ -205,23 +205,72 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(
   q[1] = make_uint2(out[2], out[3]);
 }
 
-hipError_t launch_quantize_append(int32_t fmt, const void* src, int64_t n_rows, int32_t C,
-                                  const int64_t* dst_rows, int64_t dst_start, uint8_t* codes, uint8_t* scales,
-                                  int64_t cap_rows, hipStream_t stream) {
+// ---- indexer-key rows of a paged cache: a plain copy, 16 bytes per thread.
+__global__ __launch_bounds__(256) void copy_rows_kernel(const uint4* __restrict__ src, int64_t n_rows, int32_t units,
+                                                        AppendDst dd, uint4* __restrict__ out, int64_t cap_rows) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n_rows * units) return;
+  const int64_t row = gid / units;
+  const int32_t u = (int32_t)(gid - row * units);
+  const int64_t dst = append_dst(dd, row);
+  if (dst < 0 || dst >= cap_rows) return;
+  out[dst * units + u] = src[gid];
+}
+
+// ---- window ring: position t of sequence s goes to slot t mod W (keys and values).
+__global__ __launch_bounds__(256) void ring_append_kernel(const uint4* __restrict__ k_src,
+                                                          const uint4* __restrict__ v_src, int64_t n_rows,
+                                                          int32_t units, const int32_t* __restrict__ row_seq,
+                                                          const int64_t* __restrict__ row_pos, int32_t n_seq,
+                                                          int32_t W, uint4* __restrict__ ring_k,
+                                                          uint4* __restrict__ ring_v) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n_rows * units) return;
+  const int64_t row = gid / units;
+  const int32_t u = (int32_t)(gid - row * units);
+  const int64_t s = row_seq[row], t = row_pos[row];
+  if (s < 0 || s >= n_seq || t < 0) return;
+  const int64_t dst = (s * W + t % W) * units + u;
+  ring_k[dst] = k_src[gid];
+  ring_v[dst] = v_src[gid];
+}
+
+hipError_t launch_quantize_append(int32_t fmt, const void* src, int64_t n_rows, int32_t C, const AppendDst& dst,
+                                  uint8_t* codes, uint8_t* scales, int64_t cap_rows, hipStream_t stream) {
   const uint16_t* s16 = static_cast<const uint16_t*>(src);
   if (fmt == kKvMxfp4) {
     const int64_t n = n_rows * (C >> 5);
-    quantize_mxfp4_kernel<<<dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream>>>(
-        s16, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows);
+    quantize_mxfp4_kernel<<<dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream>>>(s16, n_rows, C, dst, codes,
+                                                                                        scales, cap_rows);
   } else if (fmt == kKvFp8) {
     const int64_t n = n_rows * (C >> 4);
-    quantize_fp8_kernel<<<dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream>>>(
-        s16, n_rows, C, dst_rows, dst_start, codes, cap_rows);
+    quantize_fp8_kernel<<<dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream>>>(s16, n_rows, C, dst, codes,
+                                                                                      cap_rows);
   } else {
     const int64_t n = n_rows * (C >> 4);
-    quantize_append_kernel<<<dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream>>>(
-        s16, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows);
+    quantize_append_kernel<<<dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream>>>(s16, n_rows, C, dst, codes,
+                                                                                         scales, cap_rows);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const void* src, int64_t n_rows, int32_t width, const AppendDst& dst, void* out,
+                            int64_t cap_rows, hipStream_t stream) {
+  const int32_t units = width / 8;          // 16-byte units of a bf16 row
+  const int64_t n = n_rows * units;
+  copy_rows_kernel<<<dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream>>>(
+      static_cast<const uint4*>(src), n_rows, units, dst, static_cast<uint4*>(out), cap_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_append(const void* k_src, const void* v_src, int64_t n_rows, int32_t C, const int32_t* row_seq,
+                              const int64_t* row_pos, int32_t n_seq, int32_t W, void* ring_k, void* ring_v,
+                              hipStream_t stream) {
+  const int32_t units = C / 8;
+  const int64_t n = n_rows * units;
+  ring_append_kernel<<<dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream>>>(
+      static_cast<const uint4*>(k_src), static_cast<const uint4*>(v_src), n_rows, units, row_seq, row_pos, n_seq, W,
+      static_cast<uint4*>(ring_k), static_cast<uint4*>(ring_v));
   return hipGetLastError();
 }
 

@@ -27,19 +27,23 @@ namespace fp4kv {
 
 constexpr int kScanSteps = 16;              // 64-token steps per workgroup
 
-// Visible rows of query qi: positions 0 .. n_vis-1 of its sequence.
+// Visible rows of query qi: positions 0 .. n_vis-1 of its sequence. Paged
+// storage bounds them by max_ctx only (the block table maps every position).
+template <bool PAGED>
 __device__ __forceinline__ int64_t visible_rows(const ScanArgs& a, int qi, int64_t& base) {
-  base = a.seq_start[qi / a.q_per_seq];
+  base = PAGED ? 0 : a.seq_start[qi / a.q_per_seq];
   int64_t p = a.q_pos[qi];
   if (p < 0) return 0;                                  // sees no token
   p = p >= a.max_ctx ? a.max_ctx - 1 : p;
   int64_t n = p + 1;
-  int64_t avail = a.total_rows - base;
-  if (avail < n) n = avail;
+  if (!PAGED) {
+    int64_t avail = a.total_rows - base;
+    if (avail < n) n = avail;
+  }
   return n < 0 ? 0 : n;
 }
 
-template <int H, int D, bool REINDEX>
+template <int H, int D, bool REINDEX, bool PAGED>
 __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
   constexpr int MAXSTEPS = kScanSteps;
   constexpr int PD = 2;                       // steps of loads in flight
@@ -49,7 +53,7 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
   const int qi = blockIdx.y;
   const int lane = threadIdx.x;
   int64_t base;
-  const int64_t n_vis = visible_rows(a, qi, base);
+  const int64_t n_vis = visible_rows<PAGED>(a, qi, base);
   const int64_t first = (int64_t)blockIdx.x * a.steps * 64;
   int64_t limit;
   int32_t npool = 0;
@@ -75,14 +79,38 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
 
   const int g = lane >> 4, col = lane & 15;
   const char* seq_k = reinterpret_cast<const char*>(a.idx_k + base * D);
+  const int64_t seq = qi / a.q_per_seq;
+  // Paged Full scan: the 64 tokens of a step lie in one page (pages are >= 64
+  // rows and steps 64-aligned), so lane st holds the physical page of step st,
+  // read once here; an unmapped page reads row 0 (the block table must map
+  // every visible position).
+  int32_t step_page = -1;
+  if (PAGED && !REINDEX && lane < MAXSTEPS) {
+    const int64_t page = (first + 64 * (int64_t)lane) >> a.map.log2_page;
+    if (page < a.map.max_pages) step_page = a.map.block_table[seq * a.map.max_pages + page];
+  }
   // B operand of tile tt, k-step ks: K[token 16tt + col][32ks + 8g .. +7], loaded
   // straight into registers (64 contiguous bytes of each of 16 rows per load)
   auto load_step = [&](uint4 (&b)[4][KS], int st) {
     const int64_t s0 = first + (int64_t)st * 64;
+    int64_t prow0 = 0;
+    if (PAGED && !REINDEX) {
+      const int64_t gp = __builtin_amdgcn_readlane(step_page, st);
+      prow0 = (gp >= 0 && gp < a.map.n_pages) ? (gp << a.map.log2_page) + (s0 & ((int64_t(1) << a.map.log2_page) - 1))
+                                               : 0;
+    }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       int64_t t = position(s0 + 16 * tt + col);
       if (t < 0) t = 0;                       // any in-bounds row; its score is not used
+      if (PAGED) {
+        if (REINDEX) {
+          t = paged_row(a.map, seq, t);
+          if (t < 0) t = 0;
+        } else {
+          t = prow0 + 16 * tt + col;           // the step's rows are consecutive in its page
+        }
+      }
       const uint4* rp = reinterpret_cast<const uint4*>(seq_k + t * (D * 2));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) b[tt][ks] = rp[4 * ks + g];
@@ -171,10 +199,14 @@ static hipError_t launch_scan_hd(const ScanArgs& a, int n_q, int64_t slots, bool
   const int64_t per_wg = (int64_t)a.steps * 64;
   const int64_t gx = (slots + per_wg - 1) / per_wg;
   dim3 grid((uint32_t)gx, (uint32_t)n_q);
-  if (reindex)
-    scan_kernel<H, D, true><<<grid, dim3(64), 0, stream>>>(a);
-  else
-    scan_kernel<H, D, false><<<grid, dim3(64), 0, stream>>>(a);
+  const bool paged = a.map.block_table != nullptr;
+  if (reindex) {
+    if (paged) scan_kernel<H, D, true, true><<<grid, dim3(64), 0, stream>>>(a);
+    else scan_kernel<H, D, true, false><<<grid, dim3(64), 0, stream>>>(a);
+  } else {
+    if (paged) scan_kernel<H, D, false, true><<<grid, dim3(64), 0, stream>>>(a);
+    else scan_kernel<H, D, false, false><<<grid, dim3(64), 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

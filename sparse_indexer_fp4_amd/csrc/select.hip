@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   // histograms start at zero (the first barrier comes before any count)
   if (tid < 64) reinterpret_cast<uint4*>(sh.hist)[tid] = make_uint4(0u, 0u, 0u, 0u);
 
-  const int64_t base = a.seq_start[qi / a.q_per_seq];
+  const int64_t base = a.seq_start ? a.seq_start[qi / a.q_per_seq] : 0;   // paged storage: no base
   int64_t p = a.q_pos[qi];
   p = p >= a.max_ctx ? a.max_ctx - 1 : p;
   int64_t n_vis = p < 0 ? 0 : p + 1;                    // a negative position sees no token

@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(lib.lib, n), n
     assert sorted(lib.EXPORTS) == names
@@ -84,3 +84,25 @@ def test_kv_format_sizes_and_checks_without_gpu(lib):
     assert L.fp4kv_sparse_attn_decode_kv(2, *a) == 0                        # FP8, no queries, no scale plane
     assert L.fp4kv_sparse_attn_decode_kv(1, *a) == -1                       # MXFP4 needs scales
     assert L.fp4kv_sparse_attn_decode_kv(5, *a) == -4
+
+
+def test_paged_checks_without_gpu(lib):
+    """Page arguments are validated before anything runs: page_rows a power of two
+    in [64, 2^20], a block table, max_ctx within the table's reach."""
+    L = lib.lib
+    fake = ctypes.c_void_p(4096)
+    # fmt, kv_src, idxk_src, n_rows, C, D, row_seq, row_pos, block_table, n_seq, max_pages, page_rows, n_pages, ...
+    base = [0, fake, None, 4, 512, 0, fake, fake, fake, 2, 8]
+    tail = [fake, fake, None, None]
+    assert L.fp4kv_paged_kv_append(*base, 96, 16, *tail) == -2          # not a power of two
+    assert L.fp4kv_paged_kv_append(*base, 32, 16, *tail) == -2          # below 64
+    assert L.fp4kv_paged_kv_append(*[0, fake, None, 4, 512, 0, fake, fake, None, 2, 8], 64, 16, *tail) == -1
+    assert L.fp4kv_paged_kv_append(*[0, fake, None, 0, 512, 0, fake, fake, fake, 2, 8], 64, 16, *tail) == 0
+    assert L.fp4kv_swa_ring_append(fake, fake, 0, 512, fake, fake, 2, 128, fake, fake, None) == 0
+    assert L.fp4kv_swa_ring_append(fake, fake, 4, 512, fake, fake, 2, 0, fake, fake, None) == -2
+    # index_full_paged: max_ctx beyond max_pages * page_rows
+    out = [fake, fake, fake, fake, fake, 1 << 40, None]
+    assert L.fp4kv_index_full_paged(fake, fake, fake, fake, 2, 8, 64, 16, fake, 2, 1, 16, 128, 513, 8, 64, 32,
+                                    *out) == -2
+    assert L.fp4kv_index_full_paged(fake, fake, fake, fake, 2, 8, 64, 16, fake, 0, 1, 16, 128, 512, 8, 64, 32,
+                                    *out) == 0
