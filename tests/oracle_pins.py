@@ -282,7 +282,7 @@ def check_mxfp4_roundtrip():
 
 def check_kv_format_bytes():
     """Bytes per 512-channel row: FP4 with E4M3 per 16 = 288, MXFP4 = 256 + 16 =
-    272, FP8 = 512. FP4 is 0.5625 of FP8, the pages' "roughly half"."""
+    272, FP8 = 512. FP4 is 0.5625 of FP8, which the pages round to a half."""
     c = pages_constants()
     C = 512
     b = [kvformats.bytes_per_row(f, C) for f in (kvformats.FMT_FP4, kvformats.FMT_MXFP4, kvformats.FMT_FP8)]

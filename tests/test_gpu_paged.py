@@ -189,3 +189,60 @@ def test_paged_decode_path(fk, gpu, page_rows, fmt):
                                  bf16_to_f64(win_v[s][p + 1 - m:p + 1]), scale)
         ok, err, tol = within_tolerance(out_np[s], ro)
         assert ok, (s, err, tol)
+
+
+def test_paged_decode128k(fk, gpu):
+    """decode128k with its main KV and indexer keys in 256-row pages over a
+    permuted page pool, and its windows in rings: pools, indices and attention
+    bits equal the contiguous path for all 32 queries. Prints both paths' times."""
+    from synth import workloads as wl
+    from tests.gpu_inputs import DeviceWorkload
+    cfg = wl.CONFIGS["decode128k"]
+    _say("paged decode128k: setup")
+    dw = DeviceWorkload(cfg, gpu)
+    page_rows = 256
+    bt, n_pages = _block_tables([int(n) for n in dw.lengths], page_rows, spare=4, seed=99)
+    cache = _new_cache(fk, kvformats.FMT_FP4, bt, page_rows, n_pages, cfg.C, cfg.D, gpu)
+    starts = cfg.seq_starts()
+    for s in range(cfg.n_seq):
+        n = int(dw.lengths[s])
+        for a, b in wl.chunks(n, 1 << 16):
+            seqs = torch.full((b - a,), s, dtype=torch.int32, device=gpu)
+            poss = torch.arange(a, b, dtype=torch.int64, device=gpu)
+            fk.fp4kv_paged_kv_append(cache, seqs, poss, kv_src=wl.kv_rows_into(cfg, s, a, b, gpu),
+                                     idxk_src=dw.idx_k[int(starts[s]) + a:int(starts[s]) + b])
+    # rings holding each context's last W window rows (positions n-W .. n-1)
+    W = cfg.W
+    ring_k = torch.zeros((cfg.n_seq, W, cfg.C), dtype=torch.bfloat16, device=gpu)
+    ring_v = torch.zeros_like(ring_k)
+    seqs = torch.arange(cfg.n_seq, dtype=torch.int32, device=gpu).repeat_interleave(W)
+    poss = torch.cat([torch.arange(int(n) - W, int(n), dtype=torch.int64) for n in dw.lengths]).to(gpu)
+    fk.fp4kv_swa_ring_append(dw.swa_k[0].reshape(-1, cfg.C), dw.swa_v[0].reshape(-1, cfg.C), seqs, poss,
+                             ring_k, ring_v)
+
+    def contiguous():
+        r = fk.fp4kv_index_full(dw.idx_q[0], dw.w[0], dw.idx_k, dw.seq_start, dw.q_pos, 1, cfg.ctx, cfg.P, cfg.k)
+        o = fk.fp4kv_sparse_attn_decode(dw.q[0], dw.codes, dw.scales, dw.seq_start, r[2], r[3], dw.swa_k[0],
+                                        dw.swa_v[0], dw.q_pos, cfg.scale)
+        return r, o
+
+    def paged_path():
+        r = fk.fp4kv_index_full_paged(dw.idx_q[0], dw.w[0], cache, dw.q_pos, 1, cfg.ctx, cfg.P, cfg.k)
+        o = fk.fp4kv_sparse_attn_decode_paged(dw.q[0], cache, r[2], r[3], ring_k, ring_v, dw.q_pos, cfg.scale)
+        return r, o
+
+    (rc, oc), (rp, op) = contiguous(), paged_path()
+    torch.cuda.synchronize()
+    _say("paged decode128k: checking")
+    for a, b in zip(rc + oc, rp + op):
+        assert torch.equal(a, b)
+    for name, fn in (("contiguous", contiguous), ("paged (256-row pages, ring)", paged_path)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        _say(f"paged decode128k: {name}: index_full + attention {e0.elapsed_time(e1) / 10 * 1e3:.1f} us per call")
