@@ -350,7 +350,7 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int hg = wave >> 1, hc = wave & 1;          // head group, channel half
   const int g = lane / 16, hcol = lane % 16;
-  const int head = hg * 16 + hcol;
+  const int head = ((int)blockIdx.z * NHG + hg) * 16 + hcol;   // z: this block's group of NHG head groups
   const LanePos lp = idx_lane_load<NHG, PAGED>(a, qi, split, lane);
   const QueryInfo Q = query_info(a, qi);
   const int nchunk = Q.cs + Q.cw;
@@ -555,29 +555,41 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 
 // Splits per query for nq queries of up to `chunks` chunks: enough workgroups
 // to cover the CUs, at least two chunks per split.
-int attn_splits(int nq, int chunks) {
+// Launch plan for nq queries of Hq heads and `chunks` chunks: head groups of
+// 16 per block (nhg), blocks across the heads (hb = Hq / 16 / nhg) and splits
+// of the rows (n_split).
+struct AttnPlan {
+  int nhg, hb, n_split;
+};
+
+AttnPlan attn_plan(int nq, int Hq, int chunks) {
+  AttnPlan p;
+  p.nhg = Hq / 16;
+  p.hb = 1;
   int s = 1;
   while (s < 16 && (int64_t)nq * s < 256 && chunks >= 4 * s) s *= 2;
-  return s;
+  p.n_split = s;
+  return p;
 }
 
 size_t attn_workspace_bytes(int nq, int Hq, int k, int W) {
   const int chunks = (k + kChunk - 1) / kChunk + (W + kChunk - 1) / kChunk;
-  const int s = attn_splits(nq, chunks);
-  if (s == 1) return 0;
-  return (size_t)nq * s * Hq * (kAttnC + 2) * sizeof(float);
+  const AttnPlan p = attn_plan(nq, Hq, chunks);
+  if (p.n_split == 1) return 0;
+  return (size_t)nq * p.n_split * Hq * (kAttnC + 2) * sizeof(float);
 }
 
 hipError_t launch_attn(AttnArgs a, void* ws, hipStream_t stream) {
   if (a.nq == 0) return hipSuccess;
   const int chunks = (a.k + kChunk - 1) / kChunk + (a.W + kChunk - 1) / kChunk;
-  a.n_split = attn_splits(a.nq, chunks);
+  const AttnPlan plan = attn_plan(a.nq, a.Hq, chunks);
+  a.n_split = plan.n_split;
   if (a.n_split > 1) {
     a.part_o = static_cast<float*>(ws);
     a.part_ml = a.part_o + (size_t)a.nq * a.n_split * a.Hq * kAttnC;
   }
-  const int nhg = a.Hq / 16;
-  dim3 grid((uint32_t)a.n_split, (uint32_t)a.nq);
+  const int nhg = plan.nhg;
+  dim3 grid((uint32_t)a.n_split, (uint32_t)a.nq, (uint32_t)plan.hb);
   if (a.kv_fmt < kKvFp4 || a.kv_fmt > kKvFp8) return hipErrorInvalidValue;
   const bool paged = a.map.block_table != nullptr;
 #define FP4KV_ATTN_CASE(NH, FM)                                                                  \
