@@ -346,7 +346,10 @@ template <int NHG, int FMT, bool PAGED>
 __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   constexpr int PER = kItems / (128 * NHG);
   __shared__ AttnShared<NHG> sh;
-  const int split = blockIdx.x, qi = blockIdx.y;
+  // The query index is the fastest grid dimension: workgroups are dealt to the
+  // eight XCDs round-robin in launch order, so all splits of one query (and its
+  // combine below) run on one XCD and meet its partials in that XCD's L2.
+  const int qi = blockIdx.x, split = blockIdx.y;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int hg = wave >> 1, hc = wave & 1;          // head group, channel half
   const int g = lane / 16, hcol = lane % 16;
@@ -526,7 +529,7 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
 // a thread are in flight together.
 template <int S>
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
-  const int head = blockIdx.x, qi = blockIdx.y;
+  const int qi = blockIdx.x, head = blockIdx.y;   // query fastest, as in attn_kernel
   float2 ml[S];
   float4 v[S];
 #pragma unroll
@@ -589,7 +592,7 @@ hipError_t launch_attn(AttnArgs a, void* ws, hipStream_t stream) {
     a.part_ml = a.part_o + (size_t)a.nq * a.n_split * a.Hq * kAttnC;
   }
   const int nhg = plan.nhg;
-  dim3 grid((uint32_t)a.n_split, (uint32_t)a.nq, (uint32_t)plan.hb);
+  dim3 grid((uint32_t)a.nq, (uint32_t)a.n_split, (uint32_t)plan.hb);
   if (a.kv_fmt < kKvFp4 || a.kv_fmt > kKvFp8) return hipErrorInvalidValue;
   const bool paged = a.map.block_table != nullptr;
 #define FP4KV_ATTN_CASE(NH, FM)                                                                  \
@@ -604,7 +607,7 @@ hipError_t launch_attn(AttnArgs a, void* ws, hipStream_t stream) {
 #undef FP4KV_ATTN_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  const dim3 cgrid((uint32_t)a.Hq, (uint32_t)a.nq);
+  const dim3 cgrid((uint32_t)a.nq, (uint32_t)a.Hq);
   switch (a.n_split) {
     case 2: attn_combine_kernel<2><<<cgrid, dim3(128), 0, stream>>>(a); break;
     case 4: attn_combine_kernel<4><<<cgrid, dim3(128), 0, stream>>>(a); break;
