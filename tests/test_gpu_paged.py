@@ -117,7 +117,7 @@ def test_paged_appends_and_ring(fk, gpu, fmt):
 
 
 @pytest.mark.parametrize("page_rows", [64, 256])
-@pytest.mark.parametrize("fmt", [kvformats.FMT_FP4, kvformats.FMT_FP8], ids=["fp4", "fp8"])
+@pytest.mark.parametrize("fmt", [kvformats.FMT_FP4, kvformats.FMT_MXFP4, kvformats.FMT_FP8], ids=["fp4", "mxfp4", "fp8"])
 def test_paged_decode_path(fk, gpu, page_rows, fmt):
     """Full and Reindex indexer and decode attention through pages equal the
     contiguous path bit for bit, and the oracle."""
