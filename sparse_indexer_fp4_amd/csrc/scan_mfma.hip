@@ -12,17 +12,19 @@
 // head weights are applied there. The four 16-lane groups' partial sums of two
 // queries x two 16-token tiles are then reduce-scattered with
 // v_permlane32_swap and v_permlane16_swap so that lane l ends with the full
-// score of query l/32 at token l%32 of the 32-token half-tile.
+// score of query l/32 at token l%32 of a 32-token part of the tile.
 //
 // Workgroup = 32 queries of one sequence x one range of tokens: 8 compute waves
-// (4 queries each) and one copy wave. The copy wave streams 64-token key tiles
+// (4 queries each) and one copy wave. The copy wave streams 128-token key tiles
 // HBM -> LDS with global_load_lds into a 3-deep ring, XOR-swizzled so that the
 // compute waves' 16-byte fragment reads are free of bank conflicts. It is the
 // only wave that loads, so its vmcnt waits count its tile loads alone (the
 // compute waves' score stores never hold them up). One barrier per tile:
 // before it the copy wave has waited for the next tile and the compute waves
 // have finished the current one; the tile after next is then loaded into the
-// slot the finished tile leaves free.
+// slot the finished tile leaves free. Within a tile, each 32-token part's
+// 32 products (both query pairs) are issued before either pair's weighted
+// ReLU sums, so that one pair's vector work overlaps the other's products.
 //
 // Work items (query block, token range) are laid out so that the workgroups
 // an XCD runs together share one token range, which then streams through that
@@ -37,7 +39,7 @@ namespace fp4kv {
 constexpr int kMQ = 32;                       // queries per workgroup
 constexpr int kMWaves = 8;                    // compute waves, 4 queries each
 constexpr int kMThreads = (kMWaves + 1) * 64; // + the copy wave
-constexpr int kMTile = 64;                    // tokens per LDS tile
+constexpr int kMTile = 128;                   // tokens per LDS tile
 constexpr int kMRing = 3;                     // tiles in the ring
 
 __device__ __forceinline__ int64_t mq_visible(const ScanArgs& a, int q, int64_t base) {
@@ -137,36 +139,48 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a, MfmaSc
   }
   // visible-token limits of the queries whose scores this lane will hold (query 2jp + lane/32)
   const int32_t lim[2] = {nvis[4 * wave + (lane >> 5)], nvis[4 * wave + 2 + (lane >> 5)]};
+  float* srow[2];                             // score and block-maximum rows of query 2jp + lane/32
+  float* bmrow[2];
+#pragma unroll
+  for (int jp = 0; jp < 2; ++jp) {
+    const int64_t q = q0 + 4 * wave + 2 * jp + (lane >> 5);
+    srow[jp] = a.scores + q * a.max_ctx;
+    bmrow[jp] = a.blockmax + q * a.nblk_max;
+  }
   tile_barrier();
 
   for (int st = 0; st < nsteps; ++st) {
     const uint4* tile = ring[st % kMRing];
     const int64_t t0 = r0 + (int64_t)st * kMTile;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int part = 0; part < kMTile / 32; ++part) {
       uint4 bf[2][KS];                        // B operand: K[token col of tile tt][32ks + 8g4 .. +7]
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const int tok = 32 * half + 16 * tt + col;
+        const int tok = 32 * part + 16 * tt + col;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) bf[tt][ks] = tile[tok * NCH + ((4 * ks + g4) ^ (tok % NCH))];
       }
+      v4f acc[2][2][2];                       // [query pair jp][query of the pair][16-token tile]
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {
-        v4f acc[2][2];                        // [query of the pair][16-token tile]
+      for (int jp = 0; jp < 2; ++jp)
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) acc[qq][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+          for (int tt = 0; tt < 2; ++tt) acc[jp][qq][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
           for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
-              acc[qq][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, qa[2 * jp + qq][ks]),
-                                                                    __builtin_bit_cast(v8bf, bf[tt][ks]),
-                                                                    acc[qq][tt], 0, 0, 0);
+              acc[jp][qq][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, qa[2 * jp + qq][ks]),
+                                                                        __builtin_bit_cast(v8bf, bf[tt][ks]),
+                                                                        acc[jp][qq][tt], 0, 0, 0);
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) {
         // lane: heads 4g4..4g4+3 of token col; weighted ReLU sum over them
         float p[2][2];
 #pragma unroll
@@ -175,7 +189,7 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a, MfmaSc
           for (int tt = 0; tt < 2; ++tt) {
             float v = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v = fmaf(wv[2 * jp + qq][i], relu_f(acc[qq][tt][i]), v);
+            for (int i = 0; i < 4; ++i) v = fmaf(wv[2 * jp + qq][i], relu_f(acc[jp][qq][tt][i]), v);
             p[qq][tt] = v;
           }
         // lanes 0-31 <- query A, lanes 32-63 <- query B (head groups g, g+2 summed)
@@ -186,13 +200,11 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a, MfmaSc
         // rows of 16 lanes: (A, tile 0), (A, tile 1), (B, tile 0), (B, tile 1); all four head groups summed
         const auto yy = __builtin_amdgcn_permlane16_swap(__float_as_uint(sa), __float_as_uint(sb), false, false);
         const float y = __uint_as_float(yy[0]) + __uint_as_float(yy[1]);
-
-        const int64_t t = t0 + 32 * half + (lane & 31);
+        const int64_t t = t0 + 32 * part + (lane & 31);
         const bool vis = t < lim[jp];
-        const int64_t q = q0 + 4 * wave + 2 * jp + (lane >> 5);
-        if (vis) a.scores[q * a.max_ctx + t] = y;
+        if (vis) srow[jp][t] = y;
         const float bm = max8(vis ? y : -3.402823466e38f);
-        if ((lane & 7) == 0 && vis) a.blockmax[q * a.nblk_max + (t >> 3)] = bm;
+        if ((lane & 7) == 0 && vis) bmrow[jp][t >> 3] = bm;
       }
     }
     tile_barrier();
