@@ -13,13 +13,14 @@
 // held in registers. A longer block list is re-read from global memory in
 // each pass, in chunks of 16,384 keys where each thread again owns 16
 // consecutive keys (coalesced), and is compacted chunk by chunk. A selection of kk of the candidates is
-//   1. a radix search for the threshold key T: 8-bit digits from the highest
+//   1. a radix search for the threshold key T: 11-bit digits from the highest
 //      bit where the candidates differ down to the lowest (bits common to all
 //      candidates cost no pass, and the first pass spreads over many bins);
-//      per pass, LDS atomics into one 256-bin histogram, then one wave reads
-//      and clears the bins, finds the bin that reaches rank kk with a
-//      DPP prefix sum and broadcasts it; the search stops early when that bin
-//      holds exactly the keys still needed;
+//      per pass, LDS atomics into one 2,048-bin histogram; each thread then
+//      takes and clears two bins, one block-wide prefix sum (DPP within the
+//      wave, one barrier across waves) finds the bin that reaches rank kk, and
+//      its thread broadcasts it; the search stops early when that bin holds
+//      exactly the keys still needed;
 //   2. an ordered compaction: each run counts keys > T and == T; one
 //      block-wide prefix sum of both counts gives each run its output offset
 //      (the ties taken before a run are the lesser of the ties before it and
@@ -37,12 +38,16 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kKPT = 16;                     // keys per thread held in registers
 constexpr int kRegKeys = kSelThreads * kKPT; // 16384
+constexpr int kDigitBits = 11;               // radix digit: 2,048 bins
+constexpr int kBins = 1 << kDigitBits;
+static_assert(kBins == 2 * kSelThreads, "each thread owns two histogram bins");
 
 struct alignas(16) SelShared {
-  uint32_t hist[256];                        // digit histogram, zero between passes
+  uint32_t hist[kBins];                      // digit histogram, zero between passes
   int32_t pool[kRegKeys / 8];                // selected blocks, ascending
   int32_t out[kRegKeys];                     // selected positions, ascending
   uint32_t red[kSelWaves][4];                // per-wave partial results
+  uint32_t wsum[kSelWaves];                  // per-wave histogram counts of a radix pass
   uint32_t bc[4];                            // broadcast of the chosen bin
 };
 
@@ -135,40 +140,42 @@ __device__ void radix_threshold(SelShared& sh, const Keys& keys, int kk, uint32_
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const uint32_t diff = vor ^ vand;
   if (diff == 0) { T = vand; take_eq = kk; __syncthreads(); return; }  // all candidates equal: the first kk
-  // Only bits lo..hi differ between candidates: digits of up to 8 bits cover
-  // them from the top, so the first pass already spreads over many bins.
+  // Only bits lo..hi differ between candidates: digits of up to kDigitBits
+  // bits cover them from the top, so the first pass already spreads over many
+  // bins (integer scores below 2^20 differ in about 22 bits: two passes).
   const int hi = 31 - __clz(diff), lo = __builtin_ctz(diff);
   // bits above hi: every candidate agrees (2u << 31 wraps to 0, so hi = 31 gives an empty mask)
   uint32_t mask = ~((2u << hi) - 1u);
   uint32_t prefix = vand & mask;
   int kr = kk;
   take_eq = -1;
-  for (int top = hi; top >= lo; top -= 8) {
-    const int shift = top - 7 > lo ? top - 7 : lo;
+  for (int top = hi; top >= lo; top -= kDigitBits) {
+    const int shift = top - (kDigitBits - 1) > lo ? top - (kDigitBits - 1) : lo;
     const int width = top - shift + 1;
     const uint32_t dmask = (1u << width) - 1u;
     keys.each([&](int, uint32_t v) {
       if (v && (v & mask) == prefix) atomicAdd(&sh.hist[(v >> shift) & dmask], 1u);
     });
     __syncthreads();
-    if (wave == 0) {
-      // lane owns bins 4*lane .. 4*lane+3: reads and clears them
-      uint4* hp = reinterpret_cast<uint4*>(&sh.hist[4 * lane]);
-      const uint4 c = *hp;
-      *hp = make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t t = c.x + c.y + c.z + c.w;
-      const uint32_t incl = wave_incl_add(t);
-      uint32_t run = lane63(incl) - incl;     // keys in the bins above this lane's bins
-      const uint32_t cb[4] = {c.x, c.y, c.z, c.w};
+    // Thread t owns bins 2t and 2t+1 (higher threads own higher digits): it
+    // takes their counts and clears them, and the keys ranked above its bins
+    // are those of the higher lanes of its wave plus those of the higher waves.
+    const uint2 c = reinterpret_cast<const uint2*>(sh.hist)[threadIdx.x];
+    reinterpret_cast<uint2*>(sh.hist)[threadIdx.x] = make_uint2(0u, 0u);
+    const uint32_t t = c.x + c.y;
+    const uint32_t incl = wave_incl_add(t);
+    const uint32_t wtot = lane63(incl);
+    if (lane == 63) sh.wsum[wave] = wtot;
+    __syncthreads();
+    uint32_t above = wtot - incl;
 #pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (run < (uint32_t)kr && run + cb[j] >= (uint32_t)kr) {
-          sh.bc[0] = (uint32_t)(4 * lane + j);
-          sh.bc[1] = run;
-          sh.bc[2] = cb[j];
-        }
-        run += cb[j];
-      }
+    for (int w = kSelWaves - 1; w > 0; --w)
+      if (w > wave) above += sh.wsum[w];
+    if (above < (uint32_t)kr && above + t >= (uint32_t)kr) {   // one thread: its bins hold rank kr
+      const bool upper = above + c.y >= (uint32_t)kr;
+      sh.bc[0] = 2u * threadIdx.x + (upper ? 1u : 0u);
+      sh.bc[1] = upper ? above : above + c.y;
+      sh.bc[2] = upper ? c.y : c.x;
     }
     __syncthreads();
     const uint32_t bin = sh.bc[0];
@@ -285,7 +292,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ SelShared sh;
   const int qi = blockIdx.x, tid = threadIdx.x;
   // histograms start at zero (the first barrier comes before any count)
-  if (tid < 64) reinterpret_cast<uint4*>(sh.hist)[tid] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < kBins / 4) reinterpret_cast<uint4*>(sh.hist)[tid] = make_uint4(0u, 0u, 0u, 0u);
 
   const int64_t base = a.seq_start ? a.seq_start[qi / a.q_per_seq] : 0;   // paged storage: no base
   int64_t p = a.q_pos[qi];
