@@ -43,9 +43,12 @@ constexpr int kBins = 1 << kDigitBits;
 static_assert(kBins == 2 * kSelThreads, "each thread owns two histogram bins");
 
 struct alignas(16) SelShared {
-  uint32_t hist[kBins];                      // digit histogram, zero between passes
+  union {
+    uint32_t hist[kBins];                    // digit histogram, zero between passes
+    int32_t out[kRegKeys];                   // selected positions, ascending: written only
+                                             // after the last radix pass
+  };
   int32_t pool[kRegKeys / 8];                // selected blocks, ascending
-  int32_t out[kRegKeys];                     // selected positions, ascending
   uint32_t red[kSelWaves][4];                // per-wave partial results
   uint32_t wsum[kSelWaves];                  // per-wave histogram counts of a radix pass
   uint32_t bc[4];                            // broadcast of the chosen bin
@@ -288,7 +291,7 @@ __device__ int compact_chunks(SelShared& sh, const GlobalKeys& keys, uint32_t T,
 }
 
 template <bool REINDEX>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(kSelThreads, 8) void select_kernel(SelectArgs a) {
   __shared__ SelShared sh;
   const int qi = blockIdx.x, tid = threadIdx.x;
   // histograms start at zero (the first barrier comes before any count)
