@@ -306,6 +306,13 @@ __global__ __launch_bounds__(kSelThreads, 8) void select_kernel(SelectArgs a) {
 
   int npool;
   int32_t* pool_row = a.pool + (int64_t)qi * a.P;
+  // Lowest token key that can be selected (0: every visible pool position). A
+  // selected token's score is at least the k-th best pool block maximum, which is
+  // at least the pool's threshold key T; so when the pool holds >= k blocks, the
+  // positions scoring below T can be dropped before the token search (each pool
+  // block keeps its best token, so >= k candidates remain, and the selection is
+  // unchanged, ties included).
+  uint32_t tmin = 0u;
   if (!REINDEX) {
     // ---- blocks -> pool
     const int64_t nblk = (n_vis + 7) / 8;
@@ -331,13 +338,16 @@ __global__ __launch_bounds__(kSelThreads, 8) void select_kernel(SelectArgs a) {
       candidate_summary(sh, keys, vor, vand, cnt);
       radix_threshold(sh, keys, kk, vor, vand, T, take_eq);
       npool = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) { sh.pool[slot] = (int32_t)(i0 + j); });
+      tmin = T;
     } else if (kk > 0) {
       GlobalKeys keys{bm, nblk};
       uint32_t vor, vand, T; int cnt, take_eq;
       candidate_summary(sh, keys, vor, vand, cnt);
       radix_threshold(sh, keys, kk, vor, vand, T, take_eq);
       npool = compact_chunks(sh, keys, T, take_eq, [&](int slot, int64_t b) { sh.pool[slot] = (int32_t)b; });
+      tmin = T;
     }
+    if (npool < a.k) tmin = 0u;
     __syncthreads();
     for (int i = tid; i < a.P; i += kSelThreads) pool_row[i] = i < npool ? sh.pool[i] : -1;
     if (tid == 0) a.n_pool[qi] = npool;
@@ -373,10 +383,12 @@ __global__ __launch_bounds__(kSelThreads, 8) void select_kernel(SelectArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const bool ok = b >= 0 && b * 8 + e < n_vis;
-      keys.k[8 * half + e] = ok ? float_key(s[e]) : 0u;
+      const uint32_t key = ok ? float_key(s[e]) : 0u;
+      keys.k[8 * half + e] = key >= tmin ? key : 0u;
     }
   }
-  // float_key never gives 0 for a finite score, so the candidates are the visible positions
+  // float_key never gives 0 for a finite score, so the candidates are the visible
+  // positions (those scoring >= tmin)
   uint32_t vor, vand; int nvalid;
   candidate_summary(sh, keys, vor, vand, nvalid);
   const int kk = min(a.k, nvalid);

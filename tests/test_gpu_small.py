@@ -146,10 +146,22 @@ def test_index_full_matches_oracle(fk, gpu, lengths, H, D, P, k):
     _indexer_case(fk, gpu, lengths, H, D, P, k, seed=len(lengths) * 100 + H)
 
 
-def test_index_full_ties(fk, gpu):
-    """Tiny value range: scores tie heavily at both selection levels."""
-    _say("index_full heavy ties")
-    _indexer_case(fk, gpu, [3000, 2999, 16], 4, 64, 32, 64, seed=5, lo=-1, hi=1)
+@pytest.mark.parametrize("P,k", [
+    (32, 64),     # pool smaller than k: every visible pool position is a candidate
+    (64, 32),     # pool of >= k blocks: positions scoring below the pool threshold are dropped first
+])
+def test_index_full_ties(fk, gpu, P, k):
+    """Tiny value range: scores tie heavily at both selection levels, so the
+    k-th best position often scores exactly the pool's threshold."""
+    _say(f"index_full heavy ties P={P} k={k}")
+    _indexer_case(fk, gpu, [3000, 2999, 16], 4, 64, P, k, seed=5, lo=-1, hi=1)
+
+
+def test_index_full_all_equal_scores_pool_above_k(fk, gpu):
+    """All scores tie and the pool holds more blocks than k: the token search
+    keeps every pool position (all at the threshold) and takes the lowest."""
+    _say("index_full all-equal scores, P >= k")
+    _indexer_case(fk, gpu, [5000, 9, 130], 8, 64, 40, 16, seed=24, lo=1, hi=1)
 
 
 def test_index_full_empty_contexts(fk, gpu):
