@@ -511,15 +511,20 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
     float* op = a.out + ((int64_t)qi * a.Hq + head) * kAttnC + 256 * hc;
 #pragma unroll
     for (int t = 0; t < 16; ++t)
-      *reinterpret_cast<float4*>(op + 16 * t + 4 * g) = make_float4(o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv);
+      __builtin_nontemporal_store(v4f{o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv},
+                                  reinterpret_cast<v4f*>(op + 16 * t + 4 * g));
     if (a.lse && g == 0 && hc == 0)
       a.lse[(int64_t)qi * a.Hq + head] = l_all > 0.0f ? m_use * 0.69314718055994531f + logf(l_all) : -__builtin_inff();
   } else {
+    // Split partials are written and read back once, non-temporally, like the
+    // outputs: dirty lines left in the caches were written back during the next
+    // indexer scan and slowed it (decode step at 128K: scan 204 -> 196 us with
+    // partials and outputs non-temporal).
     const int64_t slot = ((int64_t)qi * a.n_split + split) * a.Hq + head;
     float* op = a.part_o + slot * kAttnC + 256 * hc;
 #pragma unroll
     for (int t = 0; t < 16; ++t)
-      *reinterpret_cast<float4*>(op + 16 * t + 4 * g) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
+      __builtin_nontemporal_store(v4f{o[t][0], o[t][1], o[t][2], o[t][3]}, reinterpret_cast<v4f*>(op + 16 * t + 4 * g));
     if (g == 0 && hc == 0) { a.part_ml[2 * slot] = l_all > 0.0f ? m_use : -__builtin_inff(); a.part_ml[2 * slot + 1] = l_all; }
   }
 }
@@ -536,7 +541,8 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   for (int s = 0; s < S; ++s) {
     const int64_t slot = ((int64_t)qi * S + s) * a.Hq + head;
     ml[s] = reinterpret_cast<const float2*>(a.part_ml)[slot];
-    v[s] = reinterpret_cast<const float4*>(a.part_o + slot * kAttnC)[threadIdx.x];
+    const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(a.part_o + slot * kAttnC) + threadIdx.x);
+    v[s] = make_float4(t[0], t[1], t[2], t[3]);
   }
   float M = ml[0].x;
 #pragma unroll
@@ -550,8 +556,8 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
     acc.x += f * v[s].x; acc.y += f * v[s].y; acc.z += f * v[s].z; acc.w += f * v[s].w;
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  reinterpret_cast<float4*>(a.out + ((int64_t)qi * a.Hq + head) * kAttnC)[threadIdx.x] =
-      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  __builtin_nontemporal_store(v4f{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv},
+                              reinterpret_cast<v4f*>(a.out + ((int64_t)qi * a.Hq + head) * kAttnC) + threadIdx.x);
   if (a.lse && threadIdx.x == 0)
     a.lse[(int64_t)qi * a.Hq + head] = L > 0.0f ? M * 0.69314718055994531f + logf(L) : -__builtin_inff();
 }
