@@ -14,6 +14,9 @@ One step = the whole hot path of the layer for the batch:
   fp4kv_index_select      (top-2,048 blocks -> pool -> top-512 tokens)
   fp4kv_sparse_attn_decode (FP4 gather-dequant attention + window + LSE merge)
 
+--workload tiny|chain1m|prefill|mixed times one of the other workloads instead
+(its own step, its indexer scan as the roofline kernel, no CPU baseline).
+
 --kv-format mxfp4|fp8 runs the same step over a main-KV cache in one of the
 formats the pages compare FP4 with (E2M1 + E8M0 per 32 channels; E4M3 per
 channel), appended and attended through the format-generic entry points.
@@ -139,6 +142,139 @@ def cpu_baseline(cfg, n_sample, min_seconds=10.0, kv_format="fp4"):
                       f"input generation excluded)"}
 
 
+WORKLOAD_TEXT = {
+    "tiny": "tiny: one Full-layer decode query over 4,096 tokens, indexer 4x64, pool 64 blocks, top-128, "
+            "16 heads x 512-channel FP4 latent, 128-token bf16 window",
+    "chain1m": "chain1m: 8 queries x 1,048,576-token contexts through Full, Reuse x3, Reindex, Reuse x3 "
+               "(one indexer scan, one rescoring of the pool, 8 attention layers), indexer 16x128, pool 2,048 "
+               "blocks, top-512, 64 heads x 512-channel FP4 latent, 128-token bf16 windows",
+    "prefill": "prefill: 4,096 causal queries at positions 127,000..131,095 of one 131,096-token context, "
+               "matrix-core indexer 16x128, pool 2,048 blocks, top-512, 64 heads x 512-channel FP4 latent, each "
+               "query's preceding 128 tokens as the bf16 window",
+    "mixed": "mixed: FP4 quantize-append of 65,536 rows, then a Full-layer decode of 64 queries with contexts "
+             "log-uniform in 4,096..1,048,576 tokens, indexer 16x128, pool min(2,048, blocks), top-512, 64 heads "
+             "x 512-channel FP4 latent, 128-token bf16 window",
+}
+
+
+def run_workload(args, name):
+    """One of the other workloads, timed over the launches that make up its step:
+    tiny (scores, selection, attention), chain1m (scores, selection, one Reindex,
+    8 attention layers), prefill (matrix-core scores, selection, prefill
+    attention), mixed (append of 65,536 rows, scores, selection, attention).
+    Prints one JSON line like the default run; the roofline is that of the
+    indexer scan (HBM bytes, or matrix-core FLOPs for the prefill chunk)."""
+    import numpy as np
+    import torch
+    import sparse_indexer_fp4_amd as fk
+    from synth import workloads as wl
+    from tests.gpu_inputs import DeviceWorkload
+
+    dev = torch.device("cuda:0")
+    cfg = wl.CONFIGS[name]
+    t0 = time.perf_counter()
+    log(f"generating {name} inputs on the GPU")
+    dw = DeviceWorkload(cfg, dev)
+    B = cfg.n_queries()
+    L = cfg.seq_lengths()
+    max_ctx = int(L.max()) if cfg.kind == "mixed" else cfg.ctx
+    nblk = (max_ctx + 7) // 8
+    f32, i32 = torch.float32, torch.int32
+    scores = torch.empty((B, max_ctx), dtype=f32, device=dev)
+    blockmax = torch.empty((B, nblk), dtype=f32, device=dev)
+    pool = torch.empty((B, cfg.P), dtype=i32, device=dev)
+    n_pool = torch.empty((B,), dtype=i32, device=dev)
+    idx = [torch.empty((B, cfg.k), dtype=i32, device=dev) for _ in range(2)]
+    n_idx = [torch.empty((B,), dtype=i32, device=dev) for _ in range(2)]
+    modes = cfg.modes or ("full",)
+    outs = [(torch.empty((B, cfg.Hq, cfg.C), dtype=f32, device=dev), torch.empty((B, cfg.Hq), dtype=f32, device=dev))
+            for _ in modes]
+    aws = torch.empty(max(1, fk.fp4kv_attn_workspace_bytes(B, cfg.Hq, cfg.C, cfg.k, cfg.W)), dtype=torch.uint8,
+                      device=dev)
+    rws = torch.empty(max(1, fk.fp4kv_reindex_workspace_bytes(B, cfg.P)), dtype=torch.uint8, device=dev)
+    new_x, new_dst = dw.appended_rows() if cfg.kind == "mixed" else (None, None)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    stream = torch.cuda.current_stream()
+
+    def step(scan_ev):
+        if new_x is not None:
+            fk.fp4kv_quantize_append(new_x, dw.codes, dw.scales, dst_rows=new_dst, stream=stream)
+        scan_ev[0].record(stream)
+        fk.fp4kv_index_scores(dw.idx_q[0], dw.w[0], dw.idx_k, dw.q_seq_start, dw.q_pos, dw.q_per_seq, max_ctx,
+                              scores=scores, blockmax=blockmax, stream=stream)
+        scan_ev[1].record(stream)
+        fk.fp4kv_index_select(scores, blockmax, dw.total_rows, dw.q_seq_start, dw.q_pos, dw.q_per_seq, cfg.P, cfg.k,
+                              pool_out=pool, n_pool=n_pool, idx_out=idx[0], n_idx=n_idx[0], stream=stream)
+        cur = 0
+        for layer, mode in enumerate(modes):
+            if mode == "reindex":
+                fk.fp4kv_index_reindex(dw.idx_q[layer], dw.w[layer], dw.idx_k, dw.seq_start, dw.q_pos, 1, pool,
+                                       n_pool, cfg.k, idx_out=idx[1], n_idx=n_idx[1], workspace=rws, stream=stream)
+                cur = 1
+            out, lse = outs[layer]
+            if cfg.kind == "prefill":
+                fk.fp4kv_sparse_attn_prefill(dw.q[layer], dw.codes, dw.scales, 0, idx[cur], n_idx[cur],
+                                             dw.swa_k[layer], dw.swa_v[layer], cfg.pos0, cfg.W, cfg.scale, out=out,
+                                             lse=lse, workspace=aws, stream=stream)
+            else:
+                fk.fp4kv_sparse_attn_decode(dw.q[layer], dw.codes, dw.scales, dw.seq_start, idx[cur], n_idx[cur],
+                                            dw.swa_k[layer], dw.swa_v[layer], dw.q_pos, cfg.scale, out=out, lse=lse,
+                                            workspace=aws, stream=stream)
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    warm = events()
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    evs = [events() for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t_start) / args.steps
+    scan_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+
+    # visible tokens of each query (its position + 1, within its sequence)
+    seq_of = np.zeros(B, dtype=np.int64) if cfg.kind == "prefill" else np.arange(B)
+    vis = np.minimum(cfg.q_pos().astype(np.int64) + 1, L[seq_of]).clip(min=0)
+    if cfg.kind == "prefill":
+        flops = float(vis.sum()) * cfg.H * cfg.D * 2
+        achieved = flops / (scan_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "matrix-core indexer scan (fp4kv_index_scores, 32 queries per tile)",
+                "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s", "frac": achieved / 2500.0,
+                "traffic": None, "flops_per_launch": flops}
+    else:
+        nbytes = float((vis * (cfg.D * 2 + 4) + (vis + 7) // 8 * 4).sum() + B * (cfg.H * cfg.D * 2 + cfg.H * 4))
+        achieved = nbytes / (scan_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "indexer scan (fp4kv_index_scores)", "achieved": achieved,
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                "bytes_per_launch": nbytes}
+    rec = {
+        "metric": f"queries/s, {name}",
+        "value": B / (ms_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[name], "queries": B, "max_ctx": max_ctx, "layers": len(modes),
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "detail": {"scan_ms_timed_region": scan_ms},
+        "cpu_baseline": None,
+    }
+    log(f"done in {time.perf_counter() - t0:.1f} s")
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +283,9 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=32, help="queries timed on the oracle (0: skip)")
     ap.add_argument("--kv-format", choices=sorted(KV_FORMATS), default="fp4",
                     help="main-KV cache format (default fp4: E2M1 + E4M3 per 16 channels)")
+    ap.add_argument("--workload", choices=["decode128k"] + sorted(WORKLOAD_TEXT), default="decode128k",
+                    help="decode128k (default) is the benchmark line; the others time their own step, with the "
+                         "indexer scan as the roofline kernel and no CPU baseline")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes, --steps times (calibrates "
                          "the HBM byte counters against a kernel of known traffic), then exit")
@@ -165,6 +304,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.workload != "decode128k":
+        run_workload(args, args.workload)
+        return
     if args.copy_bytes > 0:
         src = torch.ones(args.copy_bytes // 4, dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
