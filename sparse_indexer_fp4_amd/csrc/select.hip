@@ -83,16 +83,34 @@ struct RegKeys {
   }
 };
 
-// Keys of the calling thread in one 16,384-key chunk of a longer block list:
-// 16 consecutive block maxima (coalesced across the wave), key 0 past the end.
+// Keys of the calling thread's run of 16 consecutive block maxima (coalesced
+// across the wave), key 0 past the end n.
 __device__ __forceinline__ void load_run(const float* bm, int64_t n, int64_t i0, uint32_t (&k)[kKPT]) {
-  if (i0 + kKPT <= n && (((uintptr_t)(bm + i0)) & 15) == 0) {
+  // A block-maximum row starts 16-byte aligned only when the row length is a
+  // multiple of 4 (e.g. not for 131,096 tokens = 16,387 blocks). The row's
+  // misalignment m (in floats) is the same for the whole workgroup: with m != 0
+  // the run is read as two halves of three aligned 16-byte loads, each starting
+  // m floats early, if that window lies inside the row's visible blocks (else
+  // one value at a time).
+  const int m = (int)(((uintptr_t)bm >> 2) & 3);
+  if (m == 0 && i0 + kKPT <= n) {
     const float4* v = reinterpret_cast<const float4*>(bm + i0);
 #pragma unroll
     for (int j = 0; j < kKPT / 4; ++j) {
       const float4 f = v[j];
       k[4 * j] = float_key(f.x); k[4 * j + 1] = float_key(f.y);
       k[4 * j + 2] = float_key(f.z); k[4 * j + 3] = float_key(f.w);
+    }
+  } else if (m != 0 && i0 >= m && i0 - m + kKPT + 4 <= n) {
+    // two halves of 8 keys, each from three aligned loads (few live registers)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4* v = reinterpret_cast<const float4*>(bm + i0 + 8 * h - m);
+      const float4 f0 = v[0], f1 = v[1], f2 = v[2];
+      const float w[12] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w, f2.x, f2.y, f2.z, f2.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        k[8 * h + j] = float_key(m == 1 ? w[j + 1] : (m == 2 ? w[j + 2] : w[j + 3]));
     }
   } else {
 #pragma unroll
@@ -322,18 +340,7 @@ __global__ __launch_bounds__(kSelThreads, 8) void select_kernel(SelectArgs a) {
     if (kk > 0 && nblk <= kRegKeys) {
       RegKeys keys;
       const int64_t i0 = (int64_t)tid * kKPT;
-      if (i0 + kKPT <= nblk && (((uintptr_t)(bm + i0)) & 15) == 0) {
-        const float4* v = reinterpret_cast<const float4*>(bm + i0);
-#pragma unroll
-        for (int j = 0; j < kKPT / 4; ++j) {
-          const float4 f = v[j];
-          keys.k[4 * j] = float_key(f.x); keys.k[4 * j + 1] = float_key(f.y);
-          keys.k[4 * j + 2] = float_key(f.z); keys.k[4 * j + 3] = float_key(f.w);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < kKPT; ++j) keys.k[j] = i0 + j < nblk ? float_key(bm[i0 + j]) : 0u;
-      }
+      load_run(bm, nblk, i0, keys.k);
       uint32_t vor, vand, T; int cnt, take_eq;
       candidate_summary(sh, keys, vor, vand, cnt);
       radix_threshold(sh, keys, kk, vor, vand, T, take_eq);
