@@ -217,9 +217,13 @@ bool scan_supported(int H, int D) {
 // slots: max_ctx for a Full scan, P*8 for a Reindex scan.
 hipError_t launch_scan(ScanArgs a, int H, int D, int n_q, int64_t slots, bool reindex, hipStream_t stream) {
   if (n_q == 0 || slots == 0) return hipSuccess;
-  // Enough workgroups to fill 256 CUs several times over, with long runs per wave.
+  // Long runs per wave (16 steps of 64 tokens) while that still gives >= 2,048
+  // one-wave workgroups; fewer queries or slots (a Reindex over a few queries'
+  // pools, a short context) take shorter runs, down to 2 steps, so that enough
+  // waves keep loads in flight.
   const int64_t steps_total = (slots + 63) / 64;
-  const int steps = kScanSteps;
+  int steps = kScanSteps;
+  while (steps > 2 && (int64_t)n_q * ((steps_total + steps - 1) / steps) < 2048) steps /= 2;
   a.steps = steps;
 #define FP4KV_SCAN_CASE(HH, DD) \
   if (H == HH && D == DD) return launch_scan_hd<HH, DD>(a, n_q, slots, reindex, stream);
