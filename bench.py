@@ -157,6 +157,21 @@ WORKLOAD_TEXT = {
 }
 
 
+def scan_units(cfg):
+    """Algorithmic units of one indexer-scan launch over the workload's queries:
+    FLOPs for a prefill chunk (4,096 per visible (query, token) pair at 16 heads
+    x 128), otherwise HBM bytes (per visible token 2*D B of key, 4 B of score and
+    4 B per 8-token block maximum; per query its H x D bf16 query and H weights)."""
+    import numpy as np
+    L = cfg.seq_lengths()
+    B = cfg.n_queries()
+    seq_of = np.zeros(B, dtype=np.int64) if cfg.kind == "prefill" else np.arange(B)
+    vis = np.minimum(cfg.q_pos().astype(np.int64) + 1, L[seq_of]).clip(min=0)   # visible tokens per query
+    if cfg.kind == "prefill":
+        return float(vis.sum()) * cfg.H * cfg.D * 2
+    return float((vis * (cfg.D * 2 + 4) + (vis + 7) // 8 * 4).sum() + B * (cfg.H * cfg.D * 2 + cfg.H * 4))
+
+
 def run_workload(args, name):
     """One of the other workloads, timed over the launches that make up its step:
     tiny (scores, selection, attention), chain1m (scores, selection, one Reindex,
@@ -164,7 +179,6 @@ def run_workload(args, name):
     attention), mixed (append of 65,536 rows, scores, selection, attention).
     Prints one JSON line like the default run; the roofline is that of the
     indexer scan (HBM bytes, or matrix-core FLOPs for the prefill chunk)."""
-    import numpy as np
     import torch
     import sparse_indexer_fp4_amd as fk
     from synth import workloads as wl
@@ -237,17 +251,15 @@ def run_workload(args, name):
     ms_step = 1e3 * (time.perf_counter() - t_start) / args.steps
     scan_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
 
-    # visible tokens of each query (its position + 1, within its sequence)
-    seq_of = np.zeros(B, dtype=np.int64) if cfg.kind == "prefill" else np.arange(B)
-    vis = np.minimum(cfg.q_pos().astype(np.int64) + 1, L[seq_of]).clip(min=0)
+    units = scan_units(cfg)
     if cfg.kind == "prefill":
-        flops = float(vis.sum()) * cfg.H * cfg.D * 2
+        flops = units
         achieved = flops / (scan_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": "matrix-core indexer scan (fp4kv_index_scores, 32 queries per tile)",
                 "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s", "frac": achieved / 2500.0,
                 "traffic": None, "flops_per_launch": flops}
     else:
-        nbytes = float((vis * (cfg.D * 2 + 4) + (vis + 7) // 8 * 4).sum() + B * (cfg.H * cfg.D * 2 + cfg.H * 4))
+        nbytes = units
         achieved = nbytes / (scan_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "indexer scan (fp4kv_index_scores)", "achieved": achieved,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,

@@ -1,0 +1,48 @@
+"""Host-side accounting of bench.py (no GPU): the algorithmic bytes and FLOPs
+that its roofline figures divide by, checked against counts worked out by hand
+from the workload definitions."""
+import bench
+from synth import workloads as wl
+
+
+def test_decode128k_scan_bytes():
+    # 32 queries x 131,072 visible tokens x (256 B key + 4 B score) + 16,384 block
+    # maxima x 4 B, plus 16 x 128 x 2 B of query and 16 x 4 B of weights per query
+    want = 32 * (131072 * 260 + 16384 * 4 + 16 * 128 * 2 + 16 * 4)
+    assert want == 1_092_749_312
+    cfg = wl.CONFIGS["decode128k"]
+    assert bench.algorithmic_bytes(cfg)["scan"] == want
+    assert bench.scan_units(cfg) == want
+
+
+def test_prefill_scan_flops():
+    # queries at positions 127,000 .. 131,095 see position + 1 tokens each
+    pairs = sum(127_000 + i + 1 for i in range(4096))
+    assert pairs == 528_582_656
+    assert bench.scan_units(wl.CONFIGS["prefill"]) == pairs * 16 * 128 * 2
+
+
+def test_tiny_and_chain_scan_bytes():
+    # one query over 4,096 tokens, indexer 4 x 64: 128 B keys; 512 blocks
+    assert bench.scan_units(wl.CONFIGS["tiny"]) == 4096 * (128 + 4) + 512 * 4 + 4 * 64 * 2 + 4 * 4
+    # eight queries over 2^20 tokens each, indexer 16 x 128
+    n = 1 << 20
+    assert bench.scan_units(wl.CONFIGS["chain1m"]) == 8 * (n * 260 + n // 8 * 4 + 16 * 128 * 2 + 16 * 4)
+
+
+def test_mixed_scan_bytes_follow_lengths():
+    cfg = wl.CONFIGS["mixed"]
+    L = cfg.seq_lengths()
+    want = sum(int(x) * 260 + (int(x) + 7) // 8 * 4 for x in L) + len(L) * (16 * 128 * 2 + 16 * 4)
+    assert bench.scan_units(cfg) == want
+    assert all(x % 8 == 0 and 4096 <= x <= 1 << 20 for x in L)
+
+
+def test_layer_bytes_count_inputs_and_outputs_once():
+    cfg = wl.CONFIGS["decode128k"]
+    b = bench.algorithmic_bytes(cfg)
+    # attention per query: 512 FP4 rows x 288 B, 512 indices, Q 64 x 512 bf16, window K and V
+    # 2 x 128 x 512 bf16, output 64 x 512 fp32 and 64 lse
+    per_q = 512 * 288 + 512 * 4 + 64 * 512 * 2 + 2 * 128 * 512 * 2 + 64 * 512 * 4 + 64 * 4
+    assert b["attn"] == 32 * per_q
+    assert b["layer"] < b["scan"] + b["attn"] + b["select"] + b["append"]
