@@ -15,7 +15,8 @@ One step = the whole hot path of the layer for the batch:
   fp4kv_sparse_attn_decode (FP4 gather-dequant attention + window + LSE merge)
 
 --workload tiny|chain1m|prefill|mixed times one of the other workloads instead
-(its own step, its indexer scan as the roofline kernel, no CPU baseline).
+(its own step, its indexer scan as the roofline kernel, the oracle on a few
+sampled queries as the CPU baseline).
 
 --kv-format mxfp4|fp8 runs the same step over a main-KV cache in one of the
 formats the pages compare FP4 with (E2M1 + E8M0 per 32 channels; E4M3 per
@@ -157,6 +158,77 @@ WORKLOAD_TEXT = {
 }
 
 
+def cpu_baseline_workload(cfg, sample, min_seconds=10.0):
+    """The oracle, as it stands, on the sampled queries of one of the other
+    workloads: every layer of the query's schedule (Full indexer, Reindex, the
+    codec of the selected rows and attention), passes repeated until
+    min_seconds of CPU work. Input generation is not timed."""
+    import numpy as np
+    import torch
+    from synth import bf16_to_f64
+    from synth import workloads as wl
+    from tests import oracle_runner as orun
+    from oracle import attention, fp4, indexer
+
+    torch.set_num_threads(os.cpu_count() or 1)
+    modes = cfg.modes or ("full",)
+    shared_k = {}
+    prepared = []
+    for i in sample:
+        s = wl.sequence_of(cfg, i)
+        p = int(cfg.q_pos()[i])
+        if cfg.kind == "prefill":                     # one sequence: generate its keys once
+            if s not in shared_k:
+                shared_k[s] = orun.host_idx_k(cfg, s, int(cfg.seq_lengths()[s]))
+            krows = shared_k[s]
+        else:
+            krows = orun.host_idx_k(cfg, s, p + 1)
+        wpos = torch.arange(max(0, p - cfg.W + 1), p + 1, dtype=torch.int64)
+        layers = []
+        for layer, mode in enumerate(modes):
+            iq = None
+            if mode in ("full", "reindex"):
+                q, w = wl.indexer_query(cfg, layer, i)
+                iq = (bf16_to_f64(q), w.numpy().astype(np.float64))
+            layers.append((mode, iq, bf16_to_f64(wl.main_query(cfg, layer, i)),
+                           bf16_to_f64(wl.window_rows(cfg, layer, s, wpos, "k")),
+                           bf16_to_f64(wl.window_rows(cfg, layer, s, wpos, "v"))))
+        prepared.append((s, p, krows, layers))
+    t_gen = 0.0
+    done = 0
+    t0 = time.perf_counter()
+    while done == 0 or time.perf_counter() - t0 - t_gen < min_seconds:
+        for (s, p, krows, layers) in prepared:
+            pool = idx = None
+            for mode, iq, Q, wk, wv in layers:
+                if mode == "full":
+                    pool, idx, _ = indexer.index_full(iq[0], iq[1], krows, p, cfg.P, cfg.k)
+                elif mode == "reindex":
+                    idx = indexer.index_reindex(iq[0], iq[1], lambda pos: krows[pos], pool, p, cfg.k)
+                tg = time.perf_counter()
+                x = bf16_to_f64(wl.kv_rows(cfg, s, torch.from_numpy(np.asarray(idx, dtype=np.int64))))
+                t_gen += time.perf_counter() - tg
+                rows = fp4.dequantize_rows(*fp4.quantize_rows(x)) if len(idx) else np.zeros((0, cfg.C))
+                attention.attend(Q, rows, wk, wv, cfg.scale)
+            done += 1
+    dt = time.perf_counter() - t0 - t_gen
+    threads = torch.get_num_threads()
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [threads])
+    except Exception:
+        pass
+    return {"value": done / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} query evaluations ({done // len(sample)} passes over queries {list(sample)} of "
+                      f"{cfg.name}, each through its {len(modes)}-layer schedule; float64 numpy; {dt:.1f} s; "
+                      f"input generation excluded)"}
+
+
+# queries of each of the other workloads that the CPU baseline samples
+CPU_SAMPLE = {"tiny": [0], "prefill": [0, 2048, 4095], "chain1m": [0], "mixed": [0, 1, 2, 3]}
+
+
 def scan_units(cfg):
     """Algorithmic units of one indexer-scan launch over the workload's queries:
     FLOPs for a prefill chunk (4,096 per visible (query, token) pair at 16 heads
@@ -283,6 +355,9 @@ def run_workload(args, name):
         "detail": {"scan_ms_timed_region": scan_ms},
         "cpu_baseline": None,
     }
+    if args.cpu_sample > 0:
+        log(f"timing the oracle on queries {CPU_SAMPLE[name]}")
+        rec["cpu_baseline"] = cpu_baseline_workload(cfg, CPU_SAMPLE[name])
     log(f"done in {time.perf_counter() - t0:.1f} s")
     print(json.dumps(rec), flush=True)
 
@@ -297,7 +372,8 @@ def main():
                     help="main-KV cache format (default fp4: E2M1 + E4M3 per 16 channels)")
     ap.add_argument("--workload", choices=["decode128k"] + sorted(WORKLOAD_TEXT), default="decode128k",
                     help="decode128k (default) is the benchmark line; the others time their own step, with the "
-                         "indexer scan as the roofline kernel and no CPU baseline")
+                         "indexer scan as the roofline kernel and the oracle on a few sampled queries "
+                         "(--cpu-sample 0 skips it)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes, --steps times (calibrates "
                          "the HBM byte counters against a kernel of known traffic), then exit")
