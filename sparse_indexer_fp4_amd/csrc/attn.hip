@@ -563,7 +563,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 }
 
 // Splits per query for nq queries of up to `chunks` chunks: enough workgroups
-// to cover the CUs, at least two chunks per split.
+// to cover the CUs, at least one chunk per split.
 // Launch plan for nq queries of Hq heads and `chunks` chunks: head groups of
 // 16 per block (nhg), blocks across the heads (hb = Hq / 16 / nhg) and splits
 // of the rows (n_split).
@@ -576,7 +576,7 @@ AttnPlan attn_plan(int nq, int Hq, int chunks) {
   p.nhg = Hq / 16;
   p.hb = 1;
   int s = 1;
-  while (s < 16 && (int64_t)nq * s < 256 && chunks >= 4 * s) s *= 2;
+  while (s < 16 && (int64_t)nq * s < 256 && chunks >= 2 * s) s *= 2;
   p.n_split = s;
   return p;
 }
