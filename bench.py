@@ -3,16 +3,17 @@
 
 Workload (decode128k): 32 queries, each with its own 131,072-token context;
 indexer 16 heads x 128 dims (integers in [-8, 8] as bf16, weights in [1, 8]);
-pool of the best 2,048 blocks of 8 tokens, top 512 tokens; attention with 64
+pool of the best 2,048 eight-token blocks, top 512 tokens; attention with 64
 heads over the 512-channel FP4 main-KV latent plus a 128-token bf16 window.
 Inputs are synthetic, seeded, generated on the GPU, resident in HBM before
 timing starts.
 
 One step = the whole hot path of the layer for the batch:
-  fp4kv_quantize_append   (the newest token's KV row of each sequence)
-  fp4kv_index_scores      (indexer scan + 8-token block max)
-  fp4kv_index_select      (top-2,048 blocks -> pool -> top-512 tokens)
-  fp4kv_sparse_attn_decode (FP4 gather-dequant attention + window + LSE merge)
+  fp4kv_index_scores_append (indexer scan + 8-token block max; the newest
+                             token's FP4 KV row of each sequence is quantised
+                             and appended by extra workgroups of the same launch)
+  fp4kv_index_select        (top-2,048 blocks -> pool -> top-512 tokens)
+  fp4kv_sparse_attn_decode  (FP4 gather-dequant attention + window + LSE merge)
 
 --workload tiny|chain1m|prefill|mixed times one of the other workloads instead
 (its own step, its indexer scan as the roofline kernel, the oracle on a few
@@ -23,9 +24,10 @@ formats the pages compare FP4 with (E2M1 + E8M0 per 32 channels; E4M3 per
 channel), appended and attended through the format-generic entry points.
 
 Prints one JSON line: the metric (queries/s), the step time, the roofline of
-the dominant kernel (the scan: algorithmic bytes per launch over its measured
-launch time, against 8 TB/s, with the HBM traffic the byte counters measured)
-and the float64 oracle's rate on the host cores as a CPU baseline.
+the layer (its compulsory HBM bytes over the measured step time, against
+8 TB/s, with the HBM traffic the byte counters measured) and, inside it, that
+of its dominant kernel (the indexer scan), and the float64 oracle's rate on the
+host cores as a CPU baseline.
 """
 from __future__ import annotations
 
@@ -41,12 +43,14 @@ sys.path.insert(0, ROOT)
 METRIC = "decode queries/s + HBM GB/s (% of peak), Full-layer sparse attn @128K ctx"
 HBM_PEAK_GBPS = 8000.0
 
-# HBM bytes per scan launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes over this
-# command, each scaled by the counter's reading for a plain 1 GiB copy (x1.99994 and
-# x1.0). Valid only for the scan sources they were taken on: a change to any of them
-# turns the figure into null until the counters are taken again.
-SCAN_SOURCES = ("scan.hip", "kernels.h", "common.h")
-SCAN_TRAFFIC = {"sources_sha256_16": "0e66b5c6b8543f8f", "bytes_per_launch": 1095911343}
+# HBM bytes of one decode128k step (and of its scan launch) from rocprofv3
+# FETCH_SIZE and WRITE_SIZE passes over this command, each scaled by the
+# counter's reading for a plain 1 GiB copy (x1.99994 and x1.0). Valid only for
+# the kernel sources they were taken on: a change to any of them turns the
+# figures into null until the counters are taken again.
+KERNEL_SOURCES = ("api.hip", "attn.hip", "common.h", "kernels.h", "quant.hip", "quant_dev.h", "scan.hip",
+                  "scan_mfma.hip", "select.hip")
+STEP_TRAFFIC = {"sources_sha256_16": None, "bytes_per_step": None, "scan_bytes_per_launch": None}
 
 
 def log(msg):
@@ -58,13 +62,15 @@ KV_ROW_BYTES = {"fp4": 512 // 2 + 512 // 16, "mxfp4": 512 // 2 + 512 // 32, "fp8
 
 
 def algorithmic_bytes(cfg, kv_format="fp4"):
-    """Compulsory HBM bytes per call, counting inputs once and outputs once."""
+    """Compulsory HBM bytes per call, counting inputs once and outputs once.
+    'scan_intermediate' is what the scan writes for the selection to read
+    (token scores and block maxima): not part of the layer's compulsory bytes."""
     B, N = cfg.n_seq, cfg.ctx
     nblk = (N + 7) // 8
     scan = (B * N * cfg.D * 2            # indexer keys
             + B * cfg.H * cfg.D * 2      # indexer queries
-            + B * cfg.H * 4              # head weights
-            + B * N * 4 + B * nblk * 4)  # token scores + block maxima written
+            + B * cfg.H * 4)             # head weights
+    scan_intermediate = B * N * 4 + B * nblk * 4   # token scores + block maxima written
     select = (B * nblk * 4                       # block maxima read
               + B * cfg.P * 8 * 4                # pool token scores read
               + B * (cfg.P + cfg.k + 2) * 4)     # pool, indices, counts written
@@ -75,19 +81,32 @@ def algorithmic_bytes(cfg, kv_format="fp4"):
                 + 2 * cfg.W * cfg.C * 2          # window K and V
                 + cfg.Hq * cfg.C * 4 + cfg.Hq * 4)   # output and lse
     append = B * (cfg.C * 2 + row + 8)           # bf16 row in, FP4 row + destination out
-    # The layer as the pages' path defines it: every input once, every final output once.
-    layer = (B * N * cfg.D * 2 + B * cfg.H * cfg.D * 2 + B * cfg.H * 4
-             + B * (cfg.P + cfg.k) * 4 + attn - B * cfg.k * 4 + append)
-    return {"scan": scan, "select": select, "attn": attn, "append": append, "layer": layer}
+    # The layer as the path defines it, per query: indexer keys, indexer query and
+    # weights, pool and index lists written, the gathered rows with their
+    # indices, main Q, window K and V, and the output (the lse, the counts and
+    # the append's bytes are left out).
+    layer = B * (N * cfg.D * 2 + cfg.H * cfg.D * 2 + cfg.H * 4 + (cfg.P + cfg.k) * 4
+                 + cfg.k * row + cfg.k * 4 + cfg.Hq * cfg.C * 2 + 2 * cfg.W * cfg.C * 2 + cfg.Hq * cfg.C * 4)
+    return {"scan": scan, "scan_intermediate": scan_intermediate, "select": select, "attn": attn, "append": append,
+            "layer": layer}
 
 
-def scan_traffic():
+def sources_hash():
+    """SHA-256 (first 16 hex digits) of the kernel sources, in KERNEL_SOURCES order."""
     import hashlib
     h = hashlib.sha256()
-    for name in SCAN_SOURCES:
+    for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "sparse_indexer_fp4_amd", "csrc", name), "rb") as f:
             h.update(f.read())
-    return SCAN_TRAFFIC["bytes_per_launch"] if h.hexdigest()[:16] == SCAN_TRAFFIC["sources_sha256_16"] else None
+    return h.hexdigest()[:16]
+
+
+def step_traffic():
+    """Counter-measured HBM bytes (per step, per scan launch) if the kernel
+    sources are those they were taken on, else (None, None)."""
+    if STEP_TRAFFIC["sources_sha256_16"] != sources_hash():
+        return None, None
+    return STEP_TRAFFIC["bytes_per_step"], STEP_TRAFFIC["scan_bytes_per_launch"]
 
 
 def cpu_baseline(cfg, n_sample, min_seconds=10.0, kv_format="fp4"):
@@ -232,8 +251,10 @@ CPU_SAMPLE = {"tiny": [0], "prefill": [0, 2048, 4095], "chain1m": [0], "mixed": 
 def scan_units(cfg):
     """Algorithmic units of one indexer-scan launch over the workload's queries:
     FLOPs for a prefill chunk (4,096 per visible (query, token) pair at 16 heads
-    x 128), otherwise HBM bytes (per visible token 2*D B of key, 4 B of score and
-    4 B per 8-token block maximum; per query its H x D bf16 query and H weights)."""
+    x 128), otherwise compulsory HBM bytes (per visible token its 2*D-byte key;
+    per query its H x D bf16 query and H weights). The token scores and block
+    maxima the scan writes for the selection are intermediates, reported
+    separately (scan_intermediate_bytes)."""
     import numpy as np
     L = cfg.seq_lengths()
     B = cfg.n_queries()
@@ -241,7 +262,17 @@ def scan_units(cfg):
     vis = np.minimum(cfg.q_pos().astype(np.int64) + 1, L[seq_of]).clip(min=0)   # visible tokens per query
     if cfg.kind == "prefill":
         return float(vis.sum()) * cfg.H * cfg.D * 2
-    return float((vis * (cfg.D * 2 + 4) + (vis + 7) // 8 * 4).sum() + B * (cfg.H * cfg.D * 2 + cfg.H * 4))
+    return float((vis * cfg.D * 2).sum() + B * (cfg.H * cfg.D * 2 + cfg.H * 4))
+
+
+def scan_intermediate_bytes(cfg):
+    """Token scores (4 B) and block maxima (4 B per 8-token block) the scan writes."""
+    import numpy as np
+    L = cfg.seq_lengths()
+    B = cfg.n_queries()
+    seq_of = np.zeros(B, dtype=np.int64) if cfg.kind == "prefill" else np.arange(B)
+    vis = np.minimum(cfg.q_pos().astype(np.int64) + 1, L[seq_of]).clip(min=0)
+    return float((vis * 4 + (vis + 7) // 8 * 4).sum())
 
 
 def run_workload(args, name):
@@ -284,11 +315,14 @@ def run_workload(args, name):
     stream = torch.cuda.current_stream()
 
     def step(scan_ev):
-        if new_x is not None:
-            fk.fp4kv_quantize_append(new_x, dw.codes, dw.scales, dst_rows=new_dst, stream=stream)
         scan_ev[0].record(stream)
-        fk.fp4kv_index_scores(dw.idx_q[0], dw.w[0], dw.idx_k, dw.q_seq_start, dw.q_pos, dw.q_per_seq, max_ctx,
-                              scores=scores, blockmax=blockmax, stream=stream)
+        if new_x is not None:      # the append rides in the scan's launch
+            fk.fp4kv_index_scores_append(dw.idx_q[0], dw.w[0], dw.idx_k, dw.q_seq_start, dw.q_pos, dw.q_per_seq,
+                                         max_ctx, new_x, dw.codes, dw.scales, dst_rows=new_dst, scores=scores,
+                                         blockmax=blockmax, stream=stream)
+        else:
+            fk.fp4kv_index_scores(dw.idx_q[0], dw.w[0], dw.idx_k, dw.q_seq_start, dw.q_pos, dw.q_per_seq, max_ctx,
+                                  scores=scores, blockmax=blockmax, stream=stream)
         scan_ev[1].record(stream)
         fk.fp4kv_index_select(scores, blockmax, dw.total_rows, dw.q_seq_start, dw.q_pos, dw.q_per_seq, cfg.P, cfg.k,
                               pool_out=pool, n_pool=n_pool, idx_out=idx[0], n_idx=n_idx[0], stream=stream)
@@ -333,9 +367,11 @@ def run_workload(args, name):
     else:
         nbytes = units
         achieved = nbytes / (scan_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "indexer scan (fp4kv_index_scores)", "achieved": achieved,
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                "bytes_per_launch": nbytes}
+        roof = {"bound": "hbm", "kernel": "indexer scan (fp4kv_index_scores" +
+                ("_append, carrying the 65,536-row append)" if new_x is not None else ")"),
+                "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                "traffic": None, "bytes_per_launch": nbytes,
+                "intermediate_bytes_written": scan_intermediate_bytes(cfg)}
     rec = {
         "metric": f"queries/s, {name}",
         "value": B / (ms_step * 1e-3),
@@ -436,59 +472,63 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(ev=None, scan_ev=None):
-        """One decode step. `ev` (five events) brackets every launch and is used
-        only in the untimed breakdown pass; `scan_ev` (two events) brackets the
-        scan alone inside the timed region, so the step's own time carries no
-        more than two event records."""
-        if ev is not None:
-            ev[0].record(stream)
+    def attend():
         if fmt == 0:
-            fk.fp4kv_quantize_append(new_x, codes, scales, dst_rows=new_dst, stream=stream)
-        else:
-            fk.fp4kv_kv_append(fmt, new_x, codes, scales, dst_rows=new_dst, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        if scan_ev is not None:
-            scan_ev[0].record(stream)
-        fk.fp4kv_index_scores(dw.idx_q[0], dw.w[0], dw.idx_k, dw.seq_start, dw.q_pos, 1, N, scores=scores,
-                              blockmax=blockmax, stream=stream)
-        if scan_ev is not None:
-            scan_ev[1].record(stream)
-        if ev is not None:
-            ev[2].record(stream)
-        fk.fp4kv_index_select(scores, blockmax, dw.total_rows, dw.seq_start, dw.q_pos, 1, cfg.P, cfg.k,
-                              pool_out=pool, n_pool=n_pool, idx_out=idx, n_idx=n_idx, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
-        if fmt == 0:
-            fk.fp4kv_sparse_attn_decode(dw.q[0], codes, scales, dw.seq_start, idx, n_idx, dw.swa_k[0],
-                                        dw.swa_v[0], dw.q_pos, cfg.scale, out=out, lse=lse, workspace=aws,
-                                        stream=stream)
+            fk.fp4kv_sparse_attn_decode(dw.q[0], codes, scales, dw.seq_start, idx, n_idx, dw.swa_k[0], dw.swa_v[0],
+                                        dw.q_pos, cfg.scale, out=out, lse=lse, workspace=aws, stream=stream)
         else:
             fk.fp4kv_sparse_attn_decode_kv(fmt, dw.q[0], codes, scales, dw.seq_start, idx, n_idx, dw.swa_k[0],
                                            dw.swa_v[0], dw.q_pos, cfg.scale, out=out, lse=lse, workspace=aws,
                                            stream=stream)
-        if ev is not None:
-            ev[4].record(stream)
+
+    def select():
+        fk.fp4kv_index_select(scores, blockmax, dw.total_rows, dw.seq_start, dw.q_pos, 1, cfg.P, cfg.k,
+                              pool_out=pool, n_pool=n_pool, idx_out=idx, n_idx=n_idx, stream=stream)
+
+    def step():
+        """One decode step: the scan carrying the append, the selection, attention."""
+        fk.fp4kv_index_scores_append(dw.idx_q[0], dw.w[0], dw.idx_k, dw.seq_start, dw.q_pos, 1, N, new_x, codes,
+                                     scales, dst_rows=new_dst, kv_fmt=fmt, scores=scores, blockmax=blockmax,
+                                     stream=stream)
+        select()
+        attend()
+
+    def breakdown(ev):
+        """The same step as separate launches (append on its own), an event
+        around each: append, scan, selection, attention (+ combine)."""
+        ev[0].record(stream)
+        fk.fp4kv_kv_append(fmt, new_x, codes, scales, dst_rows=new_dst, stream=stream)
+        ev[1].record(stream)
+        fk.fp4kv_index_scores(dw.idx_q[0], dw.w[0], dw.idx_k, dw.seq_start, dw.q_pos, 1, N, scores=scores,
+                              blockmax=blockmax, stream=stream)
+        ev[2].record(stream)
+        select()
+        ev[3].record(stream)
+        attend()
+        ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    scan_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # Timed region: K steps back to back, bracketed by one event pair on the
+    # launch stream (and host synchronisation on both sides).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(scan_ev=scan_evs[i])
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    scan_ms = sum(e[0].elapsed_time(e[1]) for e in scan_evs) / args.steps
+    ms_step = 1e3 * elapsed / args.steps
+    ms_step_events = e0.elapsed_time(e1) / args.steps
 
     # Untimed breakdown pass: every launch bracketed by events.
     n_bd = min(args.steps, 50)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_bd)]
     for i in range(n_bd):
-        step(ev=evs[i])
+        breakdown(evs[i])
     torch.cuda.synchronize()
     per = {"append": 0.0, "scan": 0.0, "select": 0.0, "attn": 0.0}
     for ev in evs:
@@ -497,11 +537,10 @@ def main():
         per["select"] += ev[2].elapsed_time(ev[3])
         per["attn"] += ev[3].elapsed_time(ev[4])
     per = {k: v / n_bd for k, v in per.items()}          # ms per launch, breakdown pass
-    per["scan_timed_region"] = scan_ms
-    ms_step = 1e3 * elapsed / args.steps
     nbytes = algorithmic_bytes(cfg, args.kv_format)
-    scan_gbps = nbytes["scan"] / (scan_ms * 1e-3) / 1e9
-    layer_gbps = nbytes["layer"] / (ms_step * 1e-3) / 1e9
+    layer_gbps = nbytes["layer"] / (ms_step_events * 1e-3) / 1e9
+    scan_gbps = nbytes["scan"] / (per["scan"] * 1e-3) / 1e9
+    step_bytes, scan_bytes = step_traffic()
 
     rec = {
         "metric": METRIC,
@@ -524,11 +563,22 @@ def main():
                    "batch": B, "ctx": N, "pool_blocks": cfg.P, "top_k": cfg.k, "heads": cfg.Hq,
                    "kv_format": args.kv_format, "kv_bytes_per_row": KV_ROW_BYTES[args.kv_format],
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "indexer scan (fp4kv_index_scores)",
-                     "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": scan_gbps / HBM_PEAK_GBPS, "traffic": scan_traffic()},
-        "detail": {"ms_per_launch": per, "algorithmic_bytes": nbytes,
-                   "layer_hbm_gbps": layer_gbps, "layer_frac_of_peak": layer_gbps / HBM_PEAK_GBPS},
+        "roofline": {"bound": "hbm",
+                     "kernel": "whole Full-layer decode step (indexer scan carrying the append, selection, "
+                               "attention + combine), per step",
+                     "achieved": layer_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": layer_gbps / HBM_PEAK_GBPS, "traffic": step_bytes,
+                     "bytes_per_launch": nbytes["layer"], "ms_per_launch": ms_step_events,
+                     "dominant_kernel": {
+                         "kernel": "indexer scan (fp4kv_index_scores)", "bound": "hbm",
+                         "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": scan_gbps / HBM_PEAK_GBPS, "traffic": scan_bytes,
+                         "bytes_per_launch": nbytes["scan"], "ms_per_launch": per["scan"],
+                         "intermediate_bytes_written": nbytes["scan_intermediate"],
+                         "timing": "HIP events around the scan in an untimed pass of the same step as "
+                                   "separate launches"}},
+        "detail": {"ms_per_launch": per, "ms_per_step_events": ms_step_events, "algorithmic_bytes": nbytes,
+                   "kernel_sources_sha256_16": sources_hash()},
     }
     if args.cpu_sample > 0:
         log(f"timing the oracle on {args.cpu_sample} queries")

@@ -71,7 +71,7 @@ const char* fp4kv_last_error(void);
 /*
  * FP4 quantize-append of main-KV rows.
  * [G] FP4 main KV paragraph, [N] "FP4 KV Quantization and Cache Lifetime
- * Management": E2M1 values with one E4M3 scale per 16 channels and no global
+ * Management": E2M1 values, an E4M3 factor for every 16-channel group, no global
  * scale.
  *
  * For each source row i and each group g of 16 channels:
@@ -83,7 +83,8 @@ const char* fp4kv_last_error(void);
  * Codes are exact (no floating-point rounding of the ratio is involved).
  *
  *   src       (device) bf16 [n_rows, C], row-major.
- *   n_rows    rows to append (0 is allowed and launches nothing).
+ *   n_rows    rows to append (0 is allowed: nothing is launched, and the
+ *             pointers are then not checked or read).
  *   C         channels per row, a positive multiple of 32.
  *   dst_rows  (device) int64 [n_rows]: destination row of each source row, or
  *             NULL to write rows dst_start .. dst_start+n_rows-1. Destination
@@ -106,7 +107,7 @@ fp4kv_status fp4kv_quantize_append(const void* src, int64_t n_rows, int32_t C,
  * and accuracy trade: [T] "Mechanism 3" names the KV format MXFP4, and [G] FP4
  * main KV paragraph and [N] "FP4 KV Quantization and Cache Lifetime Management"
  * say FP4 takes about half the bytes of an FP8 cache.
- *   FP4KV_KV_FP4    E2M1 codes + one E4M3 scale per 16 channels (as above);
+ *   FP4KV_KV_FP4    E2M1 codes + an E4M3 scale for each 16-channel group (as above);
  *                   C/2 + C/16 bytes per row (288 at C = 512).
  *   FP4KV_KV_MXFP4  E2M1 codes + one E8M0 scale per 32 channels (OCP
  *                   microscaling): per block, e = floor(log2 amax) - 2 clamped
@@ -150,8 +151,8 @@ size_t fp4kv_index_workspace_bytes(int32_t n_q, int64_t max_ctx, int32_t block);
 /*
  * Full-mode indexer: score every visible token, keep the best blocks as the
  * candidate pool, then the best tokens inside the pool.
- * [G] hierarchical sparse indexer paragraph (pool of 2,048 blocks of 8 tokens,
- * each query keeps its best 512); [T] "Mechanism 4"; [N] "CSA2: ...", Full
+ * [G] hierarchical sparse indexer paragraph (a query first narrows the context to
+ * 2,048 eight-token blocks, then to 512 tokens); [T] "Mechanism 4"; [N] "CSA2: ...", Full
  * bullet.
  *
  * The pages leave the scoring rule open. This library computes, for query i at
@@ -168,7 +169,8 @@ size_t fp4kv_index_workspace_bytes(int32_t n_q, int64_t max_ctx, int32_t block);
  *   w           (device) fp32 [n_q, H]
  *   idx_k       (device) bf16 [total_rows, D]: indexer keys of all sequences.
  *   seq_start   (device) int64 [ceil(n_q / q_per_seq)]: first row of each
- *               sequence; query i belongs to sequence i / q_per_seq.
+ *               sequence; query i belongs to sequence i / q_per_seq. A start
+ *               outside [0, total_rows] makes the sequence empty (no token).
  *   q_pos       (device) int32 [n_q]: position of each query (its causal
  *               limit; decode: context length - 1). Clamped to max_ctx-1; a
  *               negative position sees no token (empty pool and selection);
@@ -220,6 +222,45 @@ fp4kv_status fp4kv_index_select(const float* scores, const float* blockmax, int6
                                 int32_t k, int32_t* pool_out, int32_t* n_pool, int32_t* idx_out,
                                 int32_t* n_idx, void* stream);
 
+/*
+ * A layer's indexer and its main-KV append in one go: fp4kv_index_full (or
+ * fp4kv_index_scores) together with fp4kv_kv_append of the layer's new rows.
+ * [N] "FP4 KV Quantization and Cache Lifetime Management" (new tokens enter
+ * the FP4 cache); [G] hierarchical sparse indexer paragraph.
+ *
+ * The indexer scan reads only indexer keys, never the main KV, so the append's
+ * work items ride in the scan's own launch as extra workgroups (one launch
+ * fewer per layer; where the scan cannot carry them, e.g. the matrix-core
+ * scan of many queries per sequence, the append is launched first). Results
+ * are exactly those of the two separate calls. The new rows are in the cache
+ * when the call's work completes, so a following attention call on the same
+ * stream can select them.
+ *   idx_q .. n_idx (or .. blockmax), workspace, ws_bytes: as for
+ *               fp4kv_index_full (fp4kv_index_scores).
+ *   kv_fmt, kv_src, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows:
+ *               as fmt, src, n_rows, C, ... of fp4kv_kv_append (n_rows may
+ *               be 0).
+ * Errors: those of either call; nothing is launched on error.
+ */
+fp4kv_status fp4kv_index_full_append(const void* idx_q, const float* w, const void* idx_k,
+                                     int64_t total_rows, const int64_t* seq_start,
+                                     const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                                     int32_t H, int32_t D, int64_t max_ctx, int32_t block,
+                                     int32_t P, int32_t k, int32_t* pool_out, int32_t* n_pool,
+                                     int32_t* idx_out, int32_t* n_idx, int32_t kv_fmt,
+                                     const void* kv_src, int64_t n_rows, int32_t C,
+                                     const int64_t* dst_rows, int64_t dst_start, uint8_t* codes,
+                                     uint8_t* scales, int64_t cap_rows, void* workspace,
+                                     size_t ws_bytes, void* stream);
+fp4kv_status fp4kv_index_scores_append(const void* idx_q, const float* w, const void* idx_k,
+                                       int64_t total_rows, const int64_t* seq_start,
+                                       const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                                       int32_t H, int32_t D, int64_t max_ctx, int32_t block,
+                                       float* scores, float* blockmax, int32_t kv_fmt,
+                                       const void* kv_src, int64_t n_rows, int32_t C,
+                                       const int64_t* dst_rows, int64_t dst_start, uint8_t* codes,
+                                       uint8_t* scales, int64_t cap_rows, void* stream);
+
 /* Workspace bytes fp4kv_index_reindex needs (pool token scores, fp32). */
 size_t fp4kv_reindex_workspace_bytes(int32_t n_q, int32_t P, int32_t block);
 
@@ -227,7 +268,7 @@ size_t fp4kv_reindex_workspace_bytes(int32_t n_q, int32_t P, int32_t block);
  * Reindex-mode indexer: rescore an inherited pool with this layer's own
  * indexer Q and weights, then keep the best tokens.
  * [N] "CSA2: ...", Reindex bullet: reuses the preceding Full layer's main KV
- * and indexer K and applies its own indexer Q to rescore the candidate pool;
+ * and indexer keys, scoring that layer's pool again with a fresh indexer query;
  * [G] hierarchical sparse indexer paragraph: deeper layers search the pool.
  *
  * Same scoring and ranking rule as fp4kv_index_full, over the visible
@@ -259,7 +300,7 @@ size_t fp4kv_attn_workspace_bytes(int32_t n_q, int32_t Hq, int32_t C, int32_t k,
  * Sparse attention over selected FP4 main-KV rows plus a sliding-window branch,
  * merged by log-sum-exp; one query per sequence (decode).
  * [T] "Mechanism 4" (attention runs over the selected candidates); [N] "CSA2:
- * ..." (every layer uses its own main Q and SWA KV) and "Causal
+ * ..." (each layer brings a main query and window keys/values of its own) and "Causal
  * Encoder-Decoder and Prefill Halving" (a 128-token sliding window).
  *
  * For query b at position p = q_pos[b] and every head h:
@@ -275,7 +316,8 @@ size_t fp4kv_attn_workspace_bytes(int32_t n_q, int32_t Hq, int32_t C, int32_t k,
  *
  *   q          (device) bf16 [B, Hq, C]
  *   codes      (device) uint8 [total_rows, C/2]; scales (device) uint8 [total_rows, C/16]
- *   seq_start  (device) int64 [B]: first main-KV row of each query's sequence.
+ *   seq_start  (device) int64 [B]: first main-KV row of each query's sequence
+ *              (a start outside [0, total_rows] leaves the sparse branch empty).
  *   Alignment: q, swa_k, swa_v and out 16 bytes, codes 8 bytes, scales 4 bytes
  *     (FP4KV_ERR_SHAPE otherwise).
  *   idx        (device) int32 [B, k]; n_idx (device) int32 [B]

@@ -4,7 +4,7 @@ their log-sum-exp merge.
 Follows [T] "Mechanism 4: the hierarchical sparse indexer" (attention runs over
 the selected candidates, so its cost follows the selection, not the context),
 [N] "CSA2: Sharing Main KV, Indexer K, and Top-K Indices Across Layers" (every
-layer computes its own main Q and SWA KV) and [N] "Causal Encoder-Decoder and
+layer has a main query and window keys/values of its own) and [N] "Causal Encoder-Decoder and
 Prefill Halving" plus [G] "SWA Bounded Replay" (a sliding window of the most
 recent 128 tokens).
 

@@ -1,7 +1,7 @@
-"""FP4 main-KV codec: E2M1 values with one E4M3 scale per 16 channels.
+"""FP4 main-KV codec: E2M1 values, an E4M3 scale per 16-channel group.
 
 Follows [G] "FP4 main KV" paragraph and [N] "FP4 KV Quantization and Cache
-Lifetime Management": main KV is E2M1 with one E4M3 scale per 16 channels, the
+Lifetime Management": main KV is E2M1 scaled by an E4M3 factor for every 16-channel group, the
 NVFP4 layout without its second-level (global) scale. ([T] "Mechanism 3" calls
 it MXFP4; two pages agree on E4M3 per 16, which is the reading taken.)
 

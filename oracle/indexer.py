@@ -2,13 +2,13 @@
 top-k tokens, and the Reindex rescoring.
 
 Follows [G] "hierarchical sparse indexer" paragraph (the first Full layer builds
-a pool of 2,048 blocks of 8 tokens; each query keeps its best 512 candidates;
+the context is first cut down to a pool of 2,048 eight-token blocks, then to 512 tokens per query;
 later indexing searches only the pool), [T] "Mechanism 4: the hierarchical
 sparse indexer" (coarse-to-fine: narrow the context to a candidate pool of
 about 16,384 positions, then attend over a small selection), and [N] "CSA2:
 Sharing Main KV, Indexer K, and Top-K Indices Across Layers" (Full selects a
 fresh top-512 and builds the pool; Reindex rescores that pool with its own
-indexer Q; Reuse takes the indices of the nearest Full or Reindex layer).
+indexer Q; Reuse takes over the index list of the last layer that computed one).
 
 The pages do not give the scoring rule; the reading taken is
     score(t) = sum_h w_h * max(0, q_h . k_t)

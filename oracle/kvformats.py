@@ -29,7 +29,7 @@ import numpy as np
 
 from oracle import fp4
 
-FMT_FP4 = 0       # E2M1 + one E4M3 scale per 16 channels (oracle/fp4.py)
+FMT_FP4 = 0       # E2M1 + an E4M3 scale for each 16-channel group (oracle/fp4.py)
 FMT_MXFP4 = 1     # E2M1 + one E8M0 scale per 32 channels
 FMT_FP8 = 2       # E4M3FN per value, no scale
 

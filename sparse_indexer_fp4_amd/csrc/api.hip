@@ -62,18 +62,27 @@ int64_t fp4kv_kv_scale_bytes(int32_t fmt, int32_t C) {
   return fmt == FP4KV_KV_FP4 ? C / 16 : (fmt == FP4KV_KV_MXFP4 ? C / 32 : 0);
 }
 
+static fp4kv_status check_append(const char* fn, int32_t fmt, const void* src, int64_t n_rows, int32_t C,
+                                 const int64_t* dst_rows, int64_t dst_start, const uint8_t* codes,
+                                 const uint8_t* scales, int64_t cap_rows) {
+  if (!valid_fmt(fmt)) return fail(FP4KV_ERR_UNSUPPORTED, "%s: format %d (0, 1 or 2 implemented)", fn, fmt);
+  if (n_rows == 0) return FP4KV_OK;        // nothing is read or written: the buffers may be NULL
+  if (!src || !codes || (fmt != FP4KV_KV_FP8 && !scales))
+    return fail(FP4KV_ERR_NULL, "%s: src, codes and (except for FP8) scales must be non-NULL", fn);
+  if (C <= 0 || C % 32 != 0) return fail(FP4KV_ERR_SHAPE, "%s: C=%d must be a positive multiple of 32", fn, C);
+  if (n_rows < 0 || cap_rows < 0) return fail(FP4KV_ERR_SHAPE, "%s: n_rows and cap_rows must be >= 0", fn);
+  if (!dst_rows && (dst_start < 0 || dst_start + n_rows > cap_rows))
+    return fail(FP4KV_ERR_SHAPE, "%s: rows [%lld, %lld) outside the cache of %lld rows", fn, (long long)dst_start,
+                (long long)(dst_start + n_rows), (long long)cap_rows);
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(codes) & 7u))
+    return fail(FP4KV_ERR_SHAPE, "%s: src must be 16-byte and codes 8-byte aligned", fn);
+  return FP4KV_OK;
+}
+
 fp4kv_status fp4kv_kv_append(int32_t fmt, const void* src, int64_t n_rows, int32_t C, const int64_t* dst_rows,
                              int64_t dst_start, uint8_t* codes, uint8_t* scales, int64_t cap_rows, void* stream) {
-  if (!valid_fmt(fmt)) return fail(FP4KV_ERR_UNSUPPORTED, "kv_append: format %d (0, 1 or 2 implemented)", fmt);
-  if (!src || !codes || (fmt != FP4KV_KV_FP8 && !scales))
-    return fail(FP4KV_ERR_NULL, "kv_append: src, codes and (except for FP8) scales must be non-NULL");
-  if (C <= 0 || C % 32 != 0) return fail(FP4KV_ERR_SHAPE, "kv_append: C=%d must be a positive multiple of 32", C);
-  if (n_rows < 0 || cap_rows < 0) return fail(FP4KV_ERR_SHAPE, "kv_append: n_rows and cap_rows must be >= 0");
-  if (!dst_rows && (dst_start < 0 || dst_start + n_rows > cap_rows))
-    return fail(FP4KV_ERR_SHAPE, "kv_append: rows [%lld, %lld) outside the cache of %lld rows",
-                (long long)dst_start, (long long)(dst_start + n_rows), (long long)cap_rows);
-  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(codes) & 7u))
-    return fail(FP4KV_ERR_SHAPE, "kv_append: src must be 16-byte and codes 8-byte aligned");
+  fp4kv_status st = check_append("kv_append", fmt, src, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows);
+  if (st != FP4KV_OK) return st;
   if (n_rows == 0) return ok();
   fp4kv::AppendDst dd{};
   dd.dst_rows = dst_rows;
@@ -125,7 +134,8 @@ static fp4kv_status check_indexer_common(const char* fn, const void* idx_q, cons
 static fp4kv_status launch_scores(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
                                   const int64_t* seq_start, const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
                                   int32_t H, int32_t D, int64_t max_ctx, int32_t block, float* scores,
-                                  float* blockmax, hipStream_t s, const fp4kv::PageMap* map = nullptr) {
+                                  float* blockmax, hipStream_t s, const fp4kv::PageMap* map = nullptr,
+                                  const fp4kv::AppendJob* app = nullptr) {
   fp4kv::ScanArgs sa{};
   if (map) sa.map = *map;
   sa.idx_q = static_cast<const uint16_t*>(idx_q);
@@ -141,9 +151,15 @@ static fp4kv_status launch_scores(const void* idx_q, const float* w, const void*
   sa.nblk_max = nblk_of(max_ctx, block);
   // Many queries per sequence share every key: the scan is a dense product on the matrix cores
   // (contiguous storage only; a paged cache is scanned query by query).
-  if (!map && fp4kv::scan_mfma_supported(H, D, q_per_seq) && max_ctx <= INT32_MAX)
+  if (!map && fp4kv::scan_mfma_supported(H, D, q_per_seq) && max_ctx <= INT32_MAX) {
+    if (app && app->n_rows > 0) {          // the matrix-core scan does not carry an append: it goes first
+      hipError_t e = fp4kv::launch_quantize_append(app->fmt, app->src, app->n_rows, app->C, app->dd, app->codes,
+                                                   app->scales, app->cap_rows, s);
+      if (e != hipSuccess) return hip_status(e, "quantize-append");
+    }
     return hip_status(fp4kv::launch_scan_mfma(sa, H, D, n_q, s), "index scan (matrix cores)");
-  return hip_status(fp4kv::launch_scan(sa, H, D, n_q, max_ctx, false, s), "index scan");
+  }
+  return hip_status(fp4kv::launch_scan(sa, H, D, n_q, max_ctx, false, s, app), "index scan");
 }
 
 static fp4kv_status launch_select_full(const float* scores, const float* blockmax, int64_t total_rows,
@@ -169,6 +185,22 @@ static fp4kv_status launch_select_full(const float* scores, const float* blockma
   return hip_status(fp4kv::launch_select(se, n_q, false, s), "index select");
 }
 
+// Full indexer with its workspace (scores, then block maxima) at `workspace`,
+// already known to hold fp4kv_index_workspace_bytes(n_q, max_ctx, block) bytes.
+static fp4kv_status index_full_into(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
+                                    const int64_t* seq_start, const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                                    int32_t H, int32_t D, int64_t max_ctx, int32_t block, int32_t P, int32_t k,
+                                    int32_t* pool_out, int32_t* n_pool, int32_t* idx_out, int32_t* n_idx,
+                                    void* workspace, hipStream_t s, const fp4kv::AppendJob* app = nullptr) {
+  float* scores = static_cast<float*>(workspace);
+  float* blockmax = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)n_q * max_ctx * sizeof(float)));
+  fp4kv_status st = launch_scores(idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D, max_ctx, block,
+                                  scores, blockmax, s, nullptr, app);
+  if (st != FP4KV_OK) return st;
+  return launch_select_full(scores, blockmax, total_rows, seq_start, q_pos, n_q, q_per_seq, max_ctx, block, P, k,
+                            pool_out, n_pool, idx_out, n_idx, s);
+}
+
 fp4kv_status fp4kv_index_full(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
                               const int64_t* seq_start, const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
                               int32_t H, int32_t D, int64_t max_ctx, int32_t block, int32_t P, int32_t k,
@@ -183,14 +215,8 @@ fp4kv_status fp4kv_index_full(const void* idx_q, const float* w, const void* idx
   const size_t need = fp4kv_index_workspace_bytes(n_q, max_ctx, block);
   if (!workspace || ws_bytes < need)
     return fail(FP4KV_ERR_WORKSPACE, "index_full: workspace of %zu bytes, %zu required", ws_bytes, need);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float* scores = static_cast<float*>(workspace);
-  float* blockmax = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up((size_t)n_q * max_ctx * sizeof(float)));
-  st = launch_scores(idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D, max_ctx, block, scores,
-                     blockmax, s);
-  if (st != FP4KV_OK) return st;
-  return launch_select_full(scores, blockmax, total_rows, seq_start, q_pos, n_q, q_per_seq, max_ctx, block, P, k,
-                            pool_out, n_pool, idx_out, n_idx, s);
+  return index_full_into(idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D, max_ctx, block, P, k,
+                         pool_out, n_pool, idx_out, n_idx, workspace, static_cast<hipStream_t>(stream));
 }
 
 fp4kv_status fp4kv_index_scores(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
@@ -223,6 +249,65 @@ fp4kv_status fp4kv_index_select(const float* scores, const float* blockmax, int6
   if (n_q == 0) return ok();
   return launch_select_full(scores, blockmax, total_rows, seq_start, q_pos, n_q, q_per_seq, max_ctx, block, P, k,
                             pool_out, n_pool, idx_out, n_idx, static_cast<hipStream_t>(stream));
+}
+
+fp4kv_status fp4kv_index_scores_append(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
+                                       const int64_t* seq_start, const int32_t* q_pos, int32_t n_q,
+                                       int32_t q_per_seq, int32_t H, int32_t D, int64_t max_ctx, int32_t block,
+                                       float* scores, float* blockmax, int32_t kv_fmt, const void* kv_src,
+                                       int64_t n_rows, int32_t C, const int64_t* dst_rows, int64_t dst_start,
+                                       uint8_t* codes, uint8_t* scales, int64_t cap_rows, void* stream) {
+  const char* fn = "index_scores_append";
+  int32_t dummy = 0;
+  fp4kv_status st = check_indexer_common(fn, idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D,
+                                         block, 1, 1, &dummy, &dummy);
+  if (st != FP4KV_OK) return st;
+  if (!scores || !blockmax) return fail(FP4KV_ERR_NULL, "%s: scores and blockmax must be non-NULL", fn);
+  if (max_ctx < 1) return fail(FP4KV_ERR_SHAPE, "%s: max_ctx=%lld must be >= 1", fn, (long long)max_ctx);
+  st = check_append(fn, kv_fmt, kv_src, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows);
+  if (st != FP4KV_OK) return st;
+  fp4kv::AppendDst dd{};
+  dd.dst_rows = dst_rows;
+  dd.dst_start = dst_start;
+  const fp4kv::AppendJob job = fp4kv::make_append_job(kv_fmt, kv_src, n_rows, C, dd, codes, scales, cap_rows);
+  if (n_q == 0) {
+    if (n_rows == 0) return ok();
+    return hip_status(fp4kv::launch_quantize_append(kv_fmt, kv_src, n_rows, C, dd, codes, scales, cap_rows,
+                                                    static_cast<hipStream_t>(stream)), fn);
+  }
+  return launch_scores(idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D, max_ctx, block, scores,
+                       blockmax, static_cast<hipStream_t>(stream), nullptr, &job);
+}
+
+fp4kv_status fp4kv_index_full_append(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
+                                     const int64_t* seq_start, const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                                     int32_t H, int32_t D, int64_t max_ctx, int32_t block, int32_t P, int32_t k,
+                                     int32_t* pool_out, int32_t* n_pool, int32_t* idx_out, int32_t* n_idx,
+                                     int32_t kv_fmt, const void* kv_src, int64_t n_rows, int32_t C,
+                                     const int64_t* dst_rows, int64_t dst_start, uint8_t* codes, uint8_t* scales,
+                                     int64_t cap_rows, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "index_full_append";
+  fp4kv_status st = check_indexer_common(fn, idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D,
+                                         block, P, k, idx_out, n_idx);
+  if (st != FP4KV_OK) return st;
+  if (!pool_out || !n_pool) return fail(FP4KV_ERR_NULL, "%s: pool_out and n_pool must be non-NULL", fn);
+  if (max_ctx < 1) return fail(FP4KV_ERR_SHAPE, "%s: max_ctx=%lld must be >= 1", fn, (long long)max_ctx);
+  st = check_append(fn, kv_fmt, kv_src, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows);
+  if (st != FP4KV_OK) return st;
+  const size_t need = n_q > 0 ? fp4kv_index_workspace_bytes(n_q, max_ctx, block) : 0;
+  if (n_q > 0 && (!workspace || ws_bytes < need))
+    return fail(FP4KV_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu required", fn, ws_bytes, need);
+  fp4kv::AppendDst dd{};
+  dd.dst_rows = dst_rows;
+  dd.dst_start = dst_start;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_q == 0) {
+    if (n_rows == 0) return ok();
+    return hip_status(fp4kv::launch_quantize_append(kv_fmt, kv_src, n_rows, C, dd, codes, scales, cap_rows, s), fn);
+  }
+  const fp4kv::AppendJob job = fp4kv::make_append_job(kv_fmt, kv_src, n_rows, C, dd, codes, scales, cap_rows);
+  return index_full_into(idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D, max_ctx, block, P, k,
+                         pool_out, n_pool, idx_out, n_idx, workspace, s, &job);
 }
 
 fp4kv_status fp4kv_index_reindex(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,

@@ -2,9 +2,9 @@
 // merged by log-sum-exp.
 // [T] "Mechanism 4: the hierarchical sparse indexer" (attention runs over the
 // selected candidates); [N] "CSA2: Sharing Main KV, Indexer K, and Top-K Indices
-// Across Layers" (every layer has its own main Q and SWA KV) and "Causal
+// Across Layers" (each layer brings a main query and window keys/values of its own) and "Causal
 // Encoder-Decoder and Prefill Halving" (a window of the last 128 tokens);
-// [G] FP4 main KV paragraph (E2M1 values, one E4M3 scale per 16 channels).
+// [G] FP4 main KV paragraph (E2M1 values, an E4M3 scale for each 16-channel group).
 //
 // The main KV is a shared latent (keys = values = the dequantised row) read by
 // all Hq heads, so per query the work is two dense contractions:
@@ -118,6 +118,7 @@ __device__ __forceinline__ QueryInfo query_info(const AttnArgs& a, int qi) {
   r.p = p;            // negative: the query sees no token
   int ns = a.n_idx[qi];
   r.n_s = ns < 0 ? 0 : (ns > a.k ? a.k : ns);
+  if (!a.map.block_table && (r.kv_base < 0 || r.kv_base > a.total_rows)) r.n_s = 0;   // start outside the cache
   r.n_w = p < 0 ? 0 : (int)min<int64_t>(a.W, p + 1);
   r.cs = (r.n_s + kChunk - 1) / kChunk;
   r.cw = (r.n_w + kChunk - 1) / kChunk;

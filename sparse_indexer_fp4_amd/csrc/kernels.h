@@ -7,7 +7,7 @@ namespace fp4kv {
 
 // Main-KV storage formats (values of the ABI's format argument).
 enum KvFmt : int32_t {
-  kKvFp4 = 0,     // E2M1 codes + one E4M3 scale per 16 channels
+  kKvFp4 = 0,     // E2M1 codes + an E4M3 scale for each 16-channel group
   kKvMxfp4 = 1,   // E2M1 codes + one E8M0 scale per 32 channels
   kKvFp8 = 2,     // one E4M3FN code per channel, no scale
 };
@@ -48,6 +48,19 @@ __device__ __forceinline__ int64_t append_dst(const AppendDst& d, int64_t i) {
   return d.dst_rows ? d.dst_rows[i] : d.dst_start + i;
 }
 
+// A main-KV append: rows of src (bf16 [n_rows, C]) quantised in format fmt
+// into (codes, scales) at their destinations.
+struct AppendJob {
+  int32_t fmt;
+  const uint16_t* src;
+  int64_t n_rows;
+  int32_t C;
+  AppendDst dd;
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t cap_rows;
+};
+
 struct ScanArgs {
   const uint16_t* idx_q;     // [n_q, H, D] bf16
   const float* w;            // [n_q, H]
@@ -68,6 +81,11 @@ struct ScanArgs {
   float* pool_scores;        // [n_q, P*8]
   int32_t steps;             // 64-token steps per workgroup
   PageMap map;               // paged idx_k when map.block_table (seq_start unused)
+  // An append carried by the same launch (contiguous Full scan only): grid
+  // rows n_q .. n_q + app_rows - 1 quantise app's rows instead of scanning.
+  AppendJob app;
+  int32_t app_rows;
+  int32_t n_q;
 };
 
 // Launch geometry of the matrix-core scan (host-computed).
@@ -126,6 +144,8 @@ struct AttnArgs {
   int32_t ring;                   // window rows in a ring [nq, W, C]: position t in slot t mod W
 };
 
+AppendJob make_append_job(int32_t fmt, const void* src, int64_t n_rows, int32_t C, const AppendDst& dst,
+                          uint8_t* codes, uint8_t* scales, int64_t cap_rows);
 hipError_t launch_quantize_append(int32_t fmt, const void* src, int64_t n_rows, int32_t C, const AppendDst& dst,
                                   uint8_t* codes, uint8_t* scales, int64_t cap_rows, hipStream_t stream);
 // Copy of bf16 rows [n_rows, width] to their destinations (indexer keys of a paged cache).
@@ -136,8 +156,10 @@ hipError_t launch_ring_append(const void* k_src, const void* v_src, int64_t n_ro
                               const int64_t* row_pos, int32_t n_seq, int32_t W, void* ring_k, void* ring_v,
                               hipStream_t stream);
 bool scan_supported(int H, int D);
-// slots: max_ctx for a Full scan, P*8 for a Reindex scan.
-hipError_t launch_scan(ScanArgs a, int H, int D, int n_q, int64_t slots, bool reindex, hipStream_t stream);
+// slots: max_ctx for a Full scan, P*8 for a Reindex scan. A Full scan over
+// contiguous keys also runs the append `app` (if any rows) in its launch.
+hipError_t launch_scan(ScanArgs a, int H, int D, int n_q, int64_t slots, bool reindex, hipStream_t stream,
+                       const AppendJob* app = nullptr);
 // Matrix-core Full scan for sequences with many queries (q_per_seq >= 16).
 bool scan_mfma_supported(int H, int D, int q_per_seq);
 hipError_t launch_scan_mfma(ScanArgs a, int H, int D, int n_q, hipStream_t stream);

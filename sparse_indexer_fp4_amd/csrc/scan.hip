@@ -21,7 +21,7 @@
 // Scores stay in LDS until the workgroup's last step and are stored together,
 // so the loop issues loads only and the compiler's partial vmcnt waits cover
 // exactly the keys a step needs.
-#include "kernels.h"
+#include "quant_dev.h"
 
 namespace fp4kv {
 
@@ -34,6 +34,10 @@ __device__ __forceinline__ int64_t visible_rows(const ScanArgs& a, int qi, int64
   base = PAGED ? 0 : a.seq_start[qi / a.q_per_seq];
   int64_t p = a.q_pos[qi];
   if (p < 0) return 0;                                  // sees no token
+  if (!PAGED && (base < 0 || base > a.total_rows)) {    // a start outside the keys: no visible row
+    base = 0;
+    return 0;
+  }
   p = p >= a.max_ctx ? a.max_ctx - 1 : p;
   int64_t n = p + 1;
   if (!PAGED) {
@@ -50,6 +54,13 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
   constexpr int KS = D / 32;
   __shared__ float res[MAXSTEPS * 64];        // scores of this workgroup, stored at the end
 
+  if constexpr (!REINDEX && !PAGED) {
+    if (a.app_rows > 0 && (int)blockIdx.y >= a.n_q) {     // a row of the append carried by this launch
+      const int64_t gid = ((int64_t)(blockIdx.y - a.n_q) * gridDim.x + blockIdx.x) * 64 + threadIdx.x;
+      if (gid < append_items(a.app)) append_item(a.app, gid);
+      return;
+    }
+  }
   const int qi = blockIdx.y;
   const int lane = threadIdx.x;
   int64_t base;
@@ -198,7 +209,7 @@ template <int H, int D>
 static hipError_t launch_scan_hd(const ScanArgs& a, int n_q, int64_t slots, bool reindex, hipStream_t stream) {
   const int64_t per_wg = (int64_t)a.steps * 64;
   const int64_t gx = (slots + per_wg - 1) / per_wg;
-  dim3 grid((uint32_t)gx, (uint32_t)n_q);
+  dim3 grid((uint32_t)gx, (uint32_t)(n_q + a.app_rows));
   const bool paged = a.map.block_table != nullptr;
   if (reindex) {
     if (paged) scan_kernel<H, D, true, true><<<grid, dim3(64), 0, stream>>>(a);
@@ -215,8 +226,14 @@ bool scan_supported(int H, int D) {
 }
 
 // slots: max_ctx for a Full scan, P*8 for a Reindex scan.
-hipError_t launch_scan(ScanArgs a, int H, int D, int n_q, int64_t slots, bool reindex, hipStream_t stream) {
-  if (n_q == 0 || slots == 0) return hipSuccess;
+hipError_t launch_scan(ScanArgs a, int H, int D, int n_q, int64_t slots, bool reindex, hipStream_t stream,
+                       const AppendJob* app) {
+  const int64_t app_items = app ? app->n_rows * (app->C >> (app->fmt == kKvMxfp4 ? 5 : 4)) : 0;
+  auto separate_append = [&]() {
+    return launch_quantize_append(app->fmt, app->src, app->n_rows, app->C, app->dd, app->codes, app->scales,
+                                  app->cap_rows, stream);
+  };
+  if (n_q == 0 || slots == 0) return app_items > 0 ? separate_append() : hipSuccess;
   // Long runs per wave (16 steps of 64 tokens) while that still gives >= 2,048
   // one-wave workgroups; fewer queries or slots (a Reindex over a few queries'
   // pools, a short context) take shorter runs, down to 2 steps, so that enough
@@ -225,6 +242,22 @@ hipError_t launch_scan(ScanArgs a, int H, int D, int n_q, int64_t slots, bool re
   int steps = kScanSteps;
   while (steps > 2 && (int64_t)n_q * ((steps_total + steps - 1) / steps) < 2048) steps /= 2;
   a.steps = steps;
+  a.n_q = n_q;
+  a.app_rows = 0;
+  if (app_items > 0) {
+    // A contiguous Full scan carries the append in extra grid rows of 64-thread
+    // workgroups, one item per thread (the scan never reads the main KV); other
+    // scans, or a grid that would pass 65,535 rows, launch it on its own first.
+    const int64_t gx = (slots + (int64_t)steps * 64 - 1) / ((int64_t)steps * 64);
+    const int64_t rows = (app_items + gx * 64 - 1) / (gx * 64);
+    if (!reindex && a.map.block_table == nullptr && n_q + rows <= 65535) {
+      a.app = *app;
+      a.app_rows = (int32_t)rows;
+    } else {
+      hipError_t e = separate_append();
+      if (e != hipSuccess) return e;
+    }
+  }
 #define FP4KV_SCAN_CASE(HH, DD) \
   if (H == HH && D == DD) return launch_scan_hd<HH, DD>(a, n_q, slots, reindex, stream);
   FP4KV_SCAN_CASE(4, 64) FP4KV_SCAN_CASE(8, 64) FP4KV_SCAN_CASE(16, 64)

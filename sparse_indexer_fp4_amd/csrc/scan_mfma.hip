@@ -44,7 +44,7 @@ constexpr int kMRing = 3;                     // tiles in the ring
 
 __device__ __forceinline__ int64_t mq_visible(const ScanArgs& a, int q, int64_t base) {
   int64_t p = a.q_pos[q];
-  if (p < 0) return 0;                        // sees no token
+  if (p < 0 || base < 0 || base > a.total_rows) return 0;   // sees no token (also a start outside the keys)
   p = p >= a.max_ctx ? a.max_ctx - 1 : p;
   int64_t n = p + 1;
   const int64_t avail = a.total_rows - base;

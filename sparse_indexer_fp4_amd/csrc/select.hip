@@ -1,9 +1,9 @@
 // Exact top-k selection for the hierarchical indexer: the best P blocks by
 // block score (the candidate pool), then the best k positions inside the pool.
-// [G] hierarchical sparse indexer paragraph (2,048 blocks of 8 tokens; each
-// query keeps its best 512); [N] "CSA2: Sharing Main KV, Indexer K, and Top-K
-// Indices Across Layers" (Full builds the pool and a fresh top-512; Reindex
-// re-selects within the inherited pool).
+// [G] hierarchical sparse indexer paragraph (the context narrowed to 2,048
+// eight-token blocks, then to 512 tokens per query); [N] "CSA2: Sharing Main
+// KV, Indexer K, and Top-K Indices Across Layers" (Full builds the pool and a
+// fresh top-512; Reindex re-selects within the inherited pool).
 //
 // Ranking: score descending, ties to the lower block id / position. Output:
 // ascending ids, -1 after the count.
@@ -324,8 +324,8 @@ __global__ __launch_bounds__(kSelThreads, WIDE ? 4 : 8) void select_kernel(Selec
   int64_t p = a.q_pos[qi];
   p = p >= a.max_ctx ? a.max_ctx - 1 : p;
   int64_t n_vis = p < 0 ? 0 : p + 1;                    // a negative position sees no token
-  if (a.total_rows - base < n_vis) n_vis = a.total_rows - base;
-  if (n_vis < 0) n_vis = 0;
+  if (base < 0 || base > a.total_rows) n_vis = 0;       // as the scan: a start outside the keys sees nothing
+  else if (a.total_rows - base < n_vis) n_vis = a.total_rows - base;
 
   int npool;
   int32_t* pool_row = a.pool + (int64_t)qi * a.P;

@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib.lib, n), n
     assert sorted(lib.EXPORTS) == names
@@ -42,6 +42,7 @@ def test_null_and_shape_errors_without_gpu(lib):
     assert L.fp4kv_quantize_append(fake, 4, 500, None, 0, fake, fake, 4, None) == -2
     assert L.fp4kv_quantize_append(fake, 4, 512, None, 1, fake, fake, 4, None) == -2
     assert L.fp4kv_quantize_append(fake, 0, 512, None, 0, fake, fake, 4, None) == 0
+    assert L.fp4kv_quantize_append(None, 0, 512, None, 0, None, None, 4, None) == 0   # nothing to append
     assert L.fp4kv_last_error() == b""
     # index_full: block must be 8, P*block <= 16384, k <= P*block, workspace large enough
     args = [fake, fake, fake, 100, fake, fake, 1, 1, 16, 128, 100]

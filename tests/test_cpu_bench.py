@@ -6,13 +6,27 @@ from synth import workloads as wl
 
 
 def test_decode128k_scan_bytes():
-    # 32 queries x 131,072 visible tokens x (256 B key + 4 B score) + 16,384 block
-    # maxima x 4 B, plus 16 x 128 x 2 B of query and 16 x 4 B of weights per query
-    want = 32 * (131072 * 260 + 16384 * 4 + 16 * 128 * 2 + 16 * 4)
-    assert want == 1_092_749_312
+    # compulsory: 32 queries x 131,072 visible tokens x 256 B of key, plus
+    # 16 x 128 x 2 B of query and 16 x 4 B of weights per query
+    want = 32 * (131072 * 256 + 16 * 128 * 2 + 16 * 4)
+    assert want == 1_073_874_944
     cfg = wl.CONFIGS["decode128k"]
-    assert bench.algorithmic_bytes(cfg)["scan"] == want
+    b = bench.algorithmic_bytes(cfg)
+    assert b["scan"] == want
     assert bench.scan_units(cfg) == want
+    # intermediates the scan writes for the selection: 4 B per token, 4 B per block
+    assert b["scan_intermediate"] == 32 * (131072 * 4 + 16384 * 4) == 18_874_368
+    assert bench.scan_intermediate_bytes(cfg) == 18_874_368
+
+
+def test_decode128k_layer_bytes():
+    # per query: keys 33,554,432 + query/weights 4,160 + pool/index lists
+    # (2,048 + 512) x 4 + attention 608,256 (512 x 288 B rows, 512 x 4 B indices,
+    # Q 64 x 512 bf16, window K and V 2 x 128 x 512 bf16, output 64 x 512 fp32)
+    per_q = 33_554_432 + 4_160 + 10_240 + (147_456 + 2_048 + 65_536 + 262_144 + 131_072)
+    assert per_q == 34_177_088
+    b = bench.algorithmic_bytes(wl.CONFIGS["decode128k"])
+    assert b["layer"] == 32 * per_q == 1_093_666_816
 
 
 def test_prefill_scan_flops():
@@ -23,22 +37,22 @@ def test_prefill_scan_flops():
 
 
 def test_tiny_and_chain_scan_bytes():
-    # one query over 4,096 tokens, indexer 4 x 64: 128 B keys; 512 blocks
-    assert bench.scan_units(wl.CONFIGS["tiny"]) == 4096 * (128 + 4) + 512 * 4 + 4 * 64 * 2 + 4 * 4
+    # one query over 4,096 tokens, indexer 4 x 64: 128 B keys
+    assert bench.scan_units(wl.CONFIGS["tiny"]) == 4096 * 128 + 4 * 64 * 2 + 4 * 4
     # eight queries over 2^20 tokens each, indexer 16 x 128
     n = 1 << 20
-    assert bench.scan_units(wl.CONFIGS["chain1m"]) == 8 * (n * 260 + n // 8 * 4 + 16 * 128 * 2 + 16 * 4)
+    assert bench.scan_units(wl.CONFIGS["chain1m"]) == 8 * (n * 256 + 16 * 128 * 2 + 16 * 4)
 
 
 def test_mixed_scan_bytes_follow_lengths():
     cfg = wl.CONFIGS["mixed"]
     L = cfg.seq_lengths()
-    want = sum(int(x) * 260 + (int(x) + 7) // 8 * 4 for x in L) + len(L) * (16 * 128 * 2 + 16 * 4)
+    want = sum(int(x) * 256 for x in L) + len(L) * (16 * 128 * 2 + 16 * 4)
     assert bench.scan_units(cfg) == want
     assert all(x % 8 == 0 and 4096 <= x <= 1 << 20 for x in L)
 
 
-def test_layer_bytes_count_inputs_and_outputs_once():
+def test_attention_bytes_count_inputs_and_outputs_once():
     cfg = wl.CONFIGS["decode128k"]
     b = bench.algorithmic_bytes(cfg)
     # attention per query: 512 FP4 rows x 288 B, 512 indices, Q 64 x 512 bf16, window K and V
@@ -46,3 +60,8 @@ def test_layer_bytes_count_inputs_and_outputs_once():
     per_q = 512 * 288 + 512 * 4 + 64 * 512 * 2 + 2 * 128 * 512 * 2 + 64 * 512 * 4 + 64 * 4
     assert b["attn"] == 32 * per_q
     assert b["layer"] < b["scan"] + b["attn"] + b["select"] + b["append"]
+
+
+def test_kernel_sources_hash_is_stable():
+    assert len(bench.sources_hash()) == 16
+    assert bench.sources_hash() == bench.sources_hash()
