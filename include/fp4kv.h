@@ -484,6 +484,29 @@ fp4kv_status fp4kv_sparse_attn_decode_paged(int32_t fmt, const void* q, const ui
                                             int32_t k, int32_t W, float scale, float* out, float* lse,
                                             void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * fp4kv_index_full for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, and hosts that forbid
+ * hipMalloc. Same arguments, outputs and errors as fp4kv_index_full, without
+ * the workspace: the token scores and block maxima go to a fixed 64 MiB
+ * device array inside the library (one per GPU, held until the process
+ * ends). The call itself allocates nothing.
+ *   Limit: fp4kv_index_workspace_bytes(n_q, max_ctx, block) <= 64 MiB, e.g.
+ *   32 queries at max_ctx 131,072 (18.9 MB) or 8 at 2^20 (37.7 MB); larger
+ *   calls fail with FP4KV_ERR_WORKSPACE before anything is launched.
+ *   The stream must belong to the current device (FP4KV_ERR_SHAPE otherwise).
+ *   The array is shared by every call on the same GPU and keeps the last
+ *   call's contents; nothing in it needs to start at zero. Calls that overlap
+ *   on one GPU (other streams, other threads) race on it and must be ordered
+ *   by the caller.
+ */
+fp4kv_status fp4kv_index_full_noalloc(const void* idx_q, const float* w, const void* idx_k,
+                                      int64_t total_rows, const int64_t* seq_start,
+                                      const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                                      int32_t H, int32_t D, int64_t max_ctx, int32_t block,
+                                      int32_t P, int32_t k, int32_t* pool_out, int32_t* n_pool,
+                                      int32_t* idx_out, int32_t* n_idx, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

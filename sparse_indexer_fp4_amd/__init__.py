@@ -65,6 +65,8 @@ _SIGS = {
                                        _p, _p, _p, _p, _i32, _p, _i64, _i32, _p, _i64, _p, _p, _i64, _p, _sz, _p]),
     "fp4kv_index_scores_append": (_i32, [_p, _p, _p, _i64, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _p, _p,
                                          _i32, _p, _i64, _i32, _p, _i64, _p, _p, _i64, _p]),
+    "fp4kv_index_full_noalloc": (_i32, [_p, _p, _p, _i64, _p, _p, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
+                                        _p, _p, _p, _p, _p]),
 }
 
 # Main-KV formats (FP4KV_KV_* in the header).
@@ -254,6 +256,22 @@ def fp4kv_index_scores_append(idx_q, w, idx_k, seq_start, q_pos, q_per_seq, max_
                                          _ptr(q_pos), n_q, q_per_seq, H, D, max_ctx, block, _ptr(scores),
                                          _ptr(blockmax), *app, _stream(stream)))
     return scores, blockmax
+
+
+def fp4kv_index_full_noalloc(idx_q, w, idx_k, seq_start, q_pos, q_per_seq, max_ctx, P, k, pool_out, n_pool,
+                             idx_out, n_idx, block=8, stream=None):
+    """fp4kv_index_full with the library's fixed device workspace: the caller passes
+    every output, and neither this wrapper nor the library allocates anything."""
+    n_q = idx_q.shape[0]
+    n_q, H, D = _indexer_inputs(idx_q, w, idx_k, q_pos, seq_start, _n_seq(n_q, q_per_seq))
+    _expect(pool_out, torch.int32, "pool_out", (n_q, P))
+    _expect(n_pool, torch.int32, "n_pool", (n_q,))
+    _expect(idx_out, torch.int32, "idx_out", (n_q, k))
+    _expect(n_idx, torch.int32, "n_idx", (n_q,))
+    _check(lib.fp4kv_index_full_noalloc(_ptr(idx_q), _ptr(w), _ptr(idx_k), idx_k.shape[0], _ptr(seq_start),
+                                        _ptr(q_pos), n_q, q_per_seq, H, D, max_ctx, block, P, k, _ptr(pool_out),
+                                        _ptr(n_pool), _ptr(idx_out), _ptr(n_idx), _stream(stream)))
+    return pool_out, n_pool, idx_out, n_idx
 
 
 def fp4kv_index_scores(idx_q, w, idx_k, seq_start, q_pos, q_per_seq, max_ctx, block=8, scores=None, blockmax=None,

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "fp4kv.h"
@@ -41,6 +42,47 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t nblk_of(int64_t max_ctx, int block) { return (max_ctx + block - 1) / block; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+// Workspace of fp4kv_index_full_noalloc: a device array of fixed size in this
+// code object. Each GPU the library runs on holds its own copy until the
+// process ends. Host code never passes `scratch` itself to a kernel (on the
+// host it names a stand-in, not a device address): the device address comes
+// from hipGetSymbolAddress, taken once per device below.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};   // device address of `scratch` on each device
+
+// Address of the calling device's copy of `scratch`, looked up on the first
+// call made with that device current. The stream must belong to that device.
+fp4kv_status scratch_address(const char* fn, hipStream_t s, void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(FP4KV_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+  if (s) {
+    int sdev = -1;
+    e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (sdev != dev)
+      return fail(FP4KV_ERR_SHAPE, "%s: the stream belongs to device %d, device %d is current", fn, sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, fn);
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return FP4KV_OK;
+}
 
 }  // namespace
 
@@ -665,6 +707,30 @@ fp4kv_status fp4kv_sparse_attn_decode_paged(int32_t fmt, const void* q, const ui
   a.page_q_per_seq = 1;
   a.ring = 1;
   return hip_status(fp4kv::launch_attn(a, workspace, static_cast<hipStream_t>(stream)), fn);
+}
+
+fp4kv_status fp4kv_index_full_noalloc(const void* idx_q, const float* w, const void* idx_k, int64_t total_rows,
+                                      const int64_t* seq_start, const int32_t* q_pos, int32_t n_q, int32_t q_per_seq,
+                                      int32_t H, int32_t D, int64_t max_ctx, int32_t block, int32_t P, int32_t k,
+                                      int32_t* pool_out, int32_t* n_pool, int32_t* idx_out, int32_t* n_idx,
+                                      void* stream) {
+  const char* fn = "index_full_noalloc";
+  fp4kv_status st = check_indexer_common(fn, idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D,
+                                         block, P, k, idx_out, n_idx);
+  if (st != FP4KV_OK) return st;
+  if (!pool_out || !n_pool) return fail(FP4KV_ERR_NULL, "%s: pool_out and n_pool must be non-NULL", fn);
+  if (max_ctx < 1) return fail(FP4KV_ERR_SHAPE, "%s: max_ctx=%lld must be >= 1", fn, (long long)max_ctx);
+  if (n_q == 0) return ok();
+  const size_t need = fp4kv_index_workspace_bytes(n_q, max_ctx, block);
+  if (need > kNoallocScratchBytes)
+    return fail(FP4KV_ERR_WORKSPACE, "%s: n_q=%d x max_ctx=%lld needs %zu bytes of scores, beyond the fixed %zu",
+                fn, n_q, (long long)max_ctx, need, kNoallocScratchBytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  st = scratch_address(fn, s, &ws);
+  if (st != FP4KV_OK) return st;
+  return index_full_into(idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D, max_ctx, block, P, k,
+                         pool_out, n_pool, idx_out, n_idx, ws, s);
 }
 
 }  // extern "C"

@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(lib.lib, n), n
     assert sorted(lib.EXPORTS) == names
@@ -58,6 +58,22 @@ def test_null_and_shape_errors_without_gpu(lib):
     assert L.fp4kv_sparse_attn_decode(*a, 64, 256, 8, 128, ctypes.c_float(0.1), fake, None, fake, 1 << 30, None) == -4
     assert L.fp4kv_sparse_attn_decode(*a, 48, 512, 8, 128, ctypes.c_float(0.1), fake, None, fake, 1 << 30, None) == -4
     assert L.fp4kv_sparse_attn_decode(*a, 64, 512, 0, 128, ctypes.c_float(0.1), fake, None, fake, 1 << 30, None) == -2
+
+
+def test_noalloc_limit_without_gpu(lib):
+    """The allocation-free Full indexer refuses calls whose scores would not fit its
+    fixed 64 MiB device array, before touching the device."""
+    L = lib.lib
+    fake = ctypes.c_void_p(4096)
+    out = [fake, fake, fake, fake]
+    # 64 queries x 2^20 positions of fp32 scores (256 MiB) > 64 MiB
+    assert L.fp4kv_index_full_noalloc(fake, fake, fake, 1 << 26, fake, fake, 64, 1, 16, 128, 1 << 20, 8, 2048,
+                                      512, *out, None) == -3
+    assert b"64" in L.fp4kv_last_error() or b"67108864" in L.fp4kv_last_error()
+    assert L.fp4kv_index_full_noalloc(fake, fake, fake, 1 << 26, fake, fake, 0, 1, 16, 128, 1 << 20, 8, 2048,
+                                      512, *out, None) == 0
+    assert L.fp4kv_index_full_noalloc(fake, fake, fake, 1 << 26, fake, fake, 1, 1, 16, 128, 1 << 20, 16, 2048,
+                                      512, *out, None) == -4
 
 
 def test_workspace_sizes(lib):
