@@ -8,7 +8,8 @@
 // Ranking: score descending, ties to the lower block id / position. Output:
 // ascending ids, -1 after the count.
 //
-// One 1024-thread workgroup per query. Scores map to order-preserving 32-bit
+// One 1024-thread workgroup per query and role (Full: one writes the pool, one
+// the positions, in parallel; Reindex: one). Scores map to order-preserving 32-bit
 // keys (0 = not a candidate). Each thread owns a contiguous run of 16 keys,
 // held in registers. A longer block list is re-read from global memory in
 // each pass, in chunks of 16,384 keys where each thread again owns 16
@@ -38,7 +39,7 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kKPT = 16;                     // keys per thread held in registers
 constexpr int kRegKeys = kSelThreads * kKPT; // 16384
-constexpr int kSelWideQueries = 256;         // one workgroup per query fits on MI355X's 256 CUs
+constexpr int kSelWideQueries = 256;         // workgroups that fit one per CU on MI355X's 256 CUs
 constexpr int kDigitBits = 11;               // radix digit: 2,048 bins
 constexpr int kBins = 1 << kDigitBits;
 static_assert(kBins == 2 * kSelThreads, "each thread owns two histogram bins");
@@ -337,10 +338,19 @@ __global__ __launch_bounds__(kSelThreads, WIDE ? 4 : 8) void select_kernel(Selec
   // unchanged, ties included).
   uint32_t tmin = 0u;
   if (!REINDEX) {
-    // ---- blocks -> pool
+    // ---- blocks -> pool. Two workgroups per query run side by side: role 0
+    // (blockIdx.y == 0) selects and writes the pool; role 1 selects the k
+    // positions. When the pool holds >= k blocks, role 1 needs only the k best
+    // blocks, not the whole pool: every position of the global top-k over all
+    // visible positions lies in one of them (each block ranked ahead of its
+    // block holds a distinct position ranked ahead of it: its best one, ahead
+    // on score or, on a tie, on the lower position), and that global top-k is
+    // then the pool's top-k. So role 1 ranks the blocks for a pool of
+    // min(k, blocks) and searches 8k positions instead of 8P.
+    const bool idx_role = blockIdx.y == 1;
     const int64_t nblk = (n_vis + 7) / 8;
     const float* bm = a.blockmax + (int64_t)qi * a.nblk_max;
-    const int kk = (int)min<int64_t>(a.P, nblk);
+    const int kk = (int)min<int64_t>(idx_role && a.P >= a.k ? a.k : a.P, nblk);
     npool = 0;
     if (kk > 0 && nblk <= kRegKeys) {
       RegKeys keys;
@@ -361,8 +371,11 @@ __global__ __launch_bounds__(kSelThreads, WIDE ? 4 : 8) void select_kernel(Selec
     }
     if (npool < a.k) tmin = 0u;
     __syncthreads();
-    for (int i = tid; i < a.P; i += kSelThreads) pool_row[i] = i < npool ? sh.pool[i] : -1;
-    if (tid == 0) a.n_pool[qi] = npool;
+    if (!idx_role) {
+      for (int i = tid; i < a.P; i += kSelThreads) pool_row[i] = i < npool ? sh.pool[i] : -1;
+      if (tid == 0) a.n_pool[qi] = npool;
+      return;
+    }
   } else {
     npool = a.n_pool[qi];
     npool = npool < 0 ? 0 : (npool > a.P ? a.P : npool);
@@ -420,15 +433,19 @@ __global__ __launch_bounds__(kSelThreads, WIDE ? 4 : 8) void select_kernel(Selec
 
 hipError_t launch_select(const SelectArgs& a, int n_q, bool reindex, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
-  const bool wide = n_q <= kSelWideQueries;
+  // Full: two workgroups per query (pool, positions), the query index fastest
+  // so that both land on the same XCD. Reindex: one (the pool is given).
+  const int roles = reindex ? 1 : 2;
+  const bool wide = (int64_t)n_q * roles <= kSelWideQueries;
+  const dim3 grid((uint32_t)n_q, (uint32_t)roles);
   if (reindex && wide)
-    select_kernel<true, true><<<dim3(n_q), dim3(kSelThreads), 0, stream>>>(a);
+    select_kernel<true, true><<<grid, dim3(kSelThreads), 0, stream>>>(a);
   else if (reindex)
-    select_kernel<true, false><<<dim3(n_q), dim3(kSelThreads), 0, stream>>>(a);
+    select_kernel<true, false><<<grid, dim3(kSelThreads), 0, stream>>>(a);
   else if (wide)
-    select_kernel<false, true><<<dim3(n_q), dim3(kSelThreads), 0, stream>>>(a);
+    select_kernel<false, true><<<grid, dim3(kSelThreads), 0, stream>>>(a);
   else
-    select_kernel<false, false><<<dim3(n_q), dim3(kSelThreads), 0, stream>>>(a);
+    select_kernel<false, false><<<grid, dim3(kSelThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
