@@ -86,6 +86,10 @@ struct ScanArgs {
   AppendJob app;
   int32_t app_rows;
   int32_t n_q;
+  // Work-list scan (Full, up to 512 queries): the first list_wgs workgroups of
+  // a 1-D grid walk the (query, range) list; app_wgs more carry the append.
+  int32_t list_wgs;
+  int32_t app_wgs;
 };
 
 // Launch geometry of the matrix-core scan (host-computed).

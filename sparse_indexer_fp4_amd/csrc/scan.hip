@@ -47,25 +47,16 @@ __device__ __forceinline__ int64_t visible_rows(const ScanArgs& a, int qi, int64
   return n < 0 ? 0 : n;
 }
 
+// Scores (and block maxima) of slots first .. first + steps*64 - 1 of query qi,
+// whose visible rows are positions 0 .. n_vis-1 starting at key row base (one
+// wave; res holds the range's scores until they are stored).
 template <int H, int D, bool REINDEX, bool PAGED>
-__global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
+__device__ __forceinline__ void scan_range(const ScanArgs& a, int qi, int64_t first, int64_t n_vis, int64_t base,
+                                           float* res) {
   constexpr int MAXSTEPS = kScanSteps;
   constexpr int PD = 2;                       // steps of loads in flight
   constexpr int KS = D / 32;
-  __shared__ float res[MAXSTEPS * 64];        // scores of this workgroup, stored at the end
-
-  if constexpr (!REINDEX && !PAGED) {
-    if (a.app_rows > 0 && (int)blockIdx.y >= a.n_q) {     // a row of the append carried by this launch
-      const int64_t gid = ((int64_t)(blockIdx.y - a.n_q) * gridDim.x + blockIdx.x) * 64 + threadIdx.x;
-      if (gid < append_items(a.app)) append_item(a.app, gid);
-      return;
-    }
-  }
-  const int qi = blockIdx.y;
   const int lane = threadIdx.x;
-  int64_t base;
-  const int64_t n_vis = visible_rows<PAGED>(a, qi, base);
-  const int64_t first = (int64_t)blockIdx.x * a.steps * 64;
   int64_t limit;
   int32_t npool = 0;
   const int32_t* pool = nullptr;
@@ -205,11 +196,134 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
   }
 }
 
+// The work list of a Full scan over queries of different lengths: items are
+// (query, range of steps*64 slots) over each query's visible rows only, in
+// query order. A persistent grid of list_wgs one-wave workgroups (as many as
+// the GPU holds at once) walks it, item i taken by workgroup i mod list_wgs, so
+// no workgroup is spent on a range past a short query's end. Each workgroup builds the list's prefix (first item of
+// every query) itself from q_pos and seq_start: no extra launch.
+constexpr int kListMaxQueries = 512;
+
+__device__ __forceinline__ int32_t wave_incl_sum(int32_t x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o);
+    if ((int)threadIdx.x >= o) x += y;
+  }
+  return x;
+}
+
+template <int H, int D, bool PAGED>
+__device__ __forceinline__ void scan_list(const ScanArgs& a, float* res) {
+  __shared__ int32_t item0[kListMaxQueries + 1];   // first item of each query (queries past 64)
+  const int lane = threadIdx.x;
+  const int64_t R = (int64_t)a.steps * 64;
+  int32_t carry = 0;
+  int32_t my_first = 0, my_end = 0;                // items of query `lane` (first 64 queries)
+  int64_t my_vis = 0, my_base = 0;
+  for (int c = 0; c < a.n_q; c += 64) {
+    const int q = c + lane;
+    int64_t b = 0, nv = 0;
+    if (q < a.n_q) nv = visible_rows<PAGED>(a, q, b);
+    const int32_t cnt = (int32_t)((nv + R - 1) / R);
+    const int32_t incl = wave_incl_sum(cnt);
+    if (q < a.n_q) item0[q] = carry + incl - cnt;
+    if (c == 0) {
+      my_first = carry + incl - cnt;
+      my_end = carry + incl;
+      my_vis = nv;
+      my_base = b;
+    }
+    carry += __shfl(incl, 63);
+  }
+  __syncthreads();
+  const int32_t total = carry;
+  for (int32_t item = blockIdx.x; item < total; item += a.list_wgs) {
+    int q;
+    int64_t n_vis, base;
+    if (a.n_q <= 64) {                     // the lane whose query holds the item
+      const uint64_t m = __builtin_amdgcn_ballot_w64(lane < a.n_q && my_first <= item && item < my_end);
+      if (m == 0) break;                   // (never: the queries' items partition [0, total))
+      q = (int)__builtin_ctzll(m);
+      n_vis = ((int64_t)__builtin_amdgcn_readlane((int)(my_vis >> 32), q) << 32) |
+              (uint32_t)__builtin_amdgcn_readlane((int)my_vis, q);
+      base = ((int64_t)__builtin_amdgcn_readlane((int)(my_base >> 32), q) << 32) |
+             (uint32_t)__builtin_amdgcn_readlane((int)my_base, q);
+    } else {                               // binary search: the last query whose first item is <= item
+      int lo = 0, hi = a.n_q;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (item0[mid] <= item) lo = mid;
+        else hi = mid;
+      }
+      q = __builtin_amdgcn_readfirstlane(lo);
+      n_vis = visible_rows<PAGED>(a, q, base);
+    }
+    const int32_t first_item = a.n_q <= 64 ? __builtin_amdgcn_readlane(my_first, q) : item0[q];
+    scan_range<H, D, false, PAGED>(a, q, (int64_t)(item - first_item) * R, n_vis, base, res);
+  }
+}
+
+template <int H, int D, bool REINDEX, bool PAGED>
+__global__ __launch_bounds__(64) void scan_kernel(ScanArgs a) {
+  __shared__ float res[kScanSteps * 64];        // scores of the current range, stored at its end
+  if constexpr (!REINDEX) {
+    if (a.list_wgs > 0) {
+      if ((int)blockIdx.x >= a.list_wgs) {      // workgroups of the append carried by this launch
+        if constexpr (!PAGED) {
+          const int64_t gid = (int64_t)(blockIdx.x - a.list_wgs) * 64 + threadIdx.x;
+          if (gid < append_items(a.app)) append_item(a.app, gid);
+        }
+        return;
+      }
+      scan_list<H, D, PAGED>(a, res);
+      return;
+    }
+    if constexpr (!PAGED) {
+      if (a.app_rows > 0 && (int)blockIdx.y >= a.n_q) {   // a row of the append carried by this launch
+        const int64_t gid = ((int64_t)(blockIdx.y - a.n_q) * gridDim.x + blockIdx.x) * 64 + threadIdx.x;
+        if (gid < append_items(a.app)) append_item(a.app, gid);
+        return;
+      }
+    }
+  }
+  const int qi = blockIdx.y;
+  int64_t base;
+  const int64_t n_vis = visible_rows<PAGED>(a, qi, base);
+  scan_range<H, D, REINDEX, PAGED>(a, qi, (int64_t)blockIdx.x * a.steps * 64, n_vis, base, res);
+}
+
+// Workgroups of a Full scan instance that the GPU holds resident at once
+// (occupancy per CU x CUs), asked of the runtime once per instance; the
+// work-list scan's persistent grid is that large, so every workgroup runs from
+// the start and none waits for a slot.
+template <int H, int D, bool PAGED>
+static int64_t resident_scan_wgs() {
+  static const int64_t n = [] {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return (int64_t)2048;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&scan_kernel<H, D, false, PAGED>), 64, 0) != hipSuccess ||
+        per_cu < 1)
+      return (int64_t)2048;
+    return (int64_t)cus * per_cu;
+  }();
+  return n;
+}
+
 template <int H, int D>
-static hipError_t launch_scan_hd(const ScanArgs& a, int n_q, int64_t slots, bool reindex, hipStream_t stream) {
+static hipError_t launch_scan_hd(ScanArgs a, int n_q, int64_t slots, bool reindex, hipStream_t stream) {
   const int64_t per_wg = (int64_t)a.steps * 64;
   const int64_t gx = (slots + per_wg - 1) / per_wg;
   dim3 grid((uint32_t)gx, (uint32_t)(n_q + a.app_rows));
+  if (a.list_wgs > 0) {                     // work-list scan: a persistent grid of resident workgroups
+    const int64_t upper = (int64_t)n_q * gx;
+    const int64_t res = a.map.block_table ? resident_scan_wgs<H, D, true>() : resident_scan_wgs<H, D, false>();
+    a.list_wgs = (int32_t)(upper < res ? upper : res);
+    grid = dim3((uint32_t)(a.list_wgs + a.app_wgs), 1u);
+  }
   const bool paged = a.map.block_table != nullptr;
   if (reindex) {
     if (paged) scan_kernel<H, D, true, true><<<grid, dim3(64), 0, stream>>>(a);
@@ -244,13 +358,21 @@ hipError_t launch_scan(ScanArgs a, int H, int D, int n_q, int64_t slots, bool re
   a.steps = steps;
   a.n_q = n_q;
   a.app_rows = 0;
-  if (app_items > 0) {
+  a.app_wgs = 0;
+  // A Full scan of up to kListMaxQueries queries walks a work list (see
+  // scan_list) with a persistent grid sized in launch_scan_hd; 1 marks it
+  // here. An append it carries runs in workgroups after that grid.
+  a.list_wgs = (!reindex && n_q >= 2 && n_q <= kListMaxQueries && slots <= INT32_MAX) ? 1 : 0;
+  if (a.list_wgs > 0 && app_items > 0 && a.map.block_table == nullptr) {
+    a.app = *app;
+    a.app_wgs = (int32_t)((app_items + 63) / 64);
+  } else if (app_items > 0) {
     // A contiguous Full scan carries the append in extra grid rows of 64-thread
     // workgroups, one item per thread (the scan never reads the main KV); other
     // scans, or a grid that would pass 65,535 rows, launch it on its own first.
     const int64_t gx = (slots + (int64_t)steps * 64 - 1) / ((int64_t)steps * 64);
     const int64_t rows = (app_items + gx * 64 - 1) / (gx * 64);
-    if (!reindex && a.map.block_table == nullptr && n_q + rows <= 65535) {
+    if (a.list_wgs == 0 && !reindex && a.map.block_table == nullptr && n_q + rows <= 65535) {
       a.app = *app;
       a.app_rows = (int32_t)rows;
     } else {

@@ -78,32 +78,37 @@ def test_tiny(fk, gpu):
 
 
 def test_decode128k(fk, gpu):
-    """The benchmark's workload and launch sequence (append, scores, select, attention)."""
+    """The benchmark's workload and launch sequence (scores with the append in
+    their launch, select, attention); every query against the oracle."""
     from tests.gpu_inputs import DeviceWorkload
     cfg = wl.CONFIGS["decode128k"]
     _say("decode128k: setup")
     dw = DeviceWorkload(cfg, gpu)
     new_x, new_dst = dw.newest_rows()
-    fk.fp4kv_quantize_append(new_x, dw.codes, dw.scales, dst_rows=new_dst)
-    scores, blockmax = fk.fp4kv_index_scores(dw.idx_q[0], dw.w[0], dw.idx_k, dw.seq_start, dw.q_pos, 1, cfg.ctx)
+    scores, blockmax = fk.fp4kv_index_scores_append(dw.idx_q[0], dw.w[0], dw.idx_k, dw.seq_start, dw.q_pos, 1,
+                                                    cfg.ctx, new_x, dw.codes, dw.scales, dst_rows=new_dst)
     pool, n_pool, idx, n_idx = fk.fp4kv_index_select(scores, blockmax, dw.total_rows, dw.seq_start, dw.q_pos, 1,
                                                      cfg.P, cfg.k)
     out, lse = fk.fp4kv_sparse_attn_decode(dw.q[0], dw.codes, dw.scales, dw.seq_start, idx, n_idx, dw.swa_k[0],
                                            dw.swa_v[0], dw.q_pos, cfg.scale)
     torch.cuda.synchronize()
-    _say("decode128k: checking")
+    _say("decode128k: checking all 32 queries")
     _check_cache_rows(cfg, dw)
     pool, n_pool, idx, n_idx = (t.cpu().numpy() for t in (pool, n_pool, idx, n_idx))
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
-    for i in (0, 17, 31):
+    for i in range(cfg.n_seq):
         rp, ri, s = orun.full_layer(cfg, i)
         _check_index(i, pool, n_pool, idx, n_idx, rp, ri)
-        assert np.array_equal(scores[i].cpu().numpy().astype(np.float64), s)
+        assert np.array_equal(scores[i].cpu().numpy().astype(np.float64), s), i
         _check_attn(cfg, i, 0, out, lse, ri)
-    # the same through the single-call entry point
+    # the same through the single-call entry points
     pool2, _, idx2, _ = fk.fp4kv_index_full(dw.idx_q[0], dw.w[0], dw.idx_k, dw.seq_start, dw.q_pos, 1, cfg.ctx,
                                            cfg.P, cfg.k)
     assert np.array_equal(pool2.cpu().numpy(), pool) and np.array_equal(idx2.cpu().numpy(), idx)
+    pool3, _, idx3, _ = fk.fp4kv_index_full_append(dw.idx_q[0], dw.w[0], dw.idx_k, dw.seq_start, dw.q_pos, 1,
+                                                   cfg.ctx, cfg.P, cfg.k, new_x, dw.codes, dw.scales,
+                                                   dst_rows=new_dst)
+    assert np.array_equal(pool3.cpu().numpy(), pool) and np.array_equal(idx3.cpu().numpy(), idx)
 
 
 def test_chain1m(fk, gpu):
@@ -128,7 +133,7 @@ def test_chain1m(fk, gpu):
     _say("chain1m: checking")
     _check_cache_rows(cfg, dw, 1024)
     pool_h, n_pool_h = pool.cpu().numpy(), n_pool.cpu().numpy()
-    for i in (0, 7):
+    for i in range(cfg.n_seq):
         rp, ri, _ = orun.full_layer(cfg, i)
         _check_index(i, pool_h, n_pool_h, idx.cpu().numpy(), n_idx.cpu().numpy(), rp, ri)
         rri = orun.reindex_layer(cfg, i, 4, rp)
@@ -155,7 +160,9 @@ def test_prefill(fk, gpu):
     pool, n_pool, idx, n_idx = (t.cpu().numpy() for t in (pool, n_pool, idx, n_idx))
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
     k_rows = orun.host_idx_k(cfg, 0, cfg.ctx)
-    for i in (0, 1, 2048, 4095):
+    # every in-block offset of the first and the last 32-query block of the
+    # matrix-core scan, and one query in the middle
+    for i in list(range(32)) + [2048] + list(range(cfg.T - 32, cfg.T)):
         rp, ri, _ = orun.full_layer(cfg, i, k_rows=k_rows)
         _check_index(i, pool, n_pool, idx, n_idx, rp, ri)
         _check_attn(cfg, i, 0, out, lse, ri)
@@ -169,10 +176,11 @@ def test_mixed(fk, gpu):
     _say("mixed: setup")
     dw = DeviceWorkload(cfg, gpu)
     x, dst = dw.appended_rows()
-    fk.fp4kv_quantize_append(x, dw.codes, dw.scales, dst_rows=dst)
     max_ctx = int(cfg.seq_lengths().max())
-    pool, n_pool, idx, n_idx = fk.fp4kv_index_full(dw.idx_q[0], dw.w[0], dw.idx_k, dw.seq_start, dw.q_pos, 1,
-                                                   max_ctx, cfg.P, cfg.k)
+    # the 65,536-row append rides in the indexer scan's launch, as in the benchmark
+    pool, n_pool, idx, n_idx = fk.fp4kv_index_full_append(dw.idx_q[0], dw.w[0], dw.idx_k, dw.seq_start, dw.q_pos,
+                                                          1, max_ctx, cfg.P, cfg.k, x, dw.codes, dw.scales,
+                                                          dst_rows=dst)
     out, lse = fk.fp4kv_sparse_attn_decode(dw.q[0], dw.codes, dw.scales, dw.seq_start, idx, n_idx, dw.swa_k[0],
                                            dw.swa_v[0], dw.q_pos, cfg.scale)
     torch.cuda.synchronize()
@@ -188,7 +196,27 @@ def test_mixed(fk, gpu):
     L = cfg.seq_lengths()
     pool, n_pool, idx, n_idx = (t.cpu().numpy() for t in (pool, n_pool, idx, n_idx))
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
-    for i in sorted({int(np.argmin(L)), int(np.argmax(L)), 5, 40}):
+    for i in sorted({int(np.argmin(L)), int(np.argmax(L))} | set(range(0, 64, 5))):
         rp, ri, _ = orun.full_layer(cfg, i)
         _check_index(i, pool, n_pool, idx, n_idx, rp, ri)
         _check_attn(cfg, i, 0, out, lse, ri)
+
+
+def test_prefill_matrix_core_scan_equals_per_query_scan(fk, gpu):
+    """At full prefill size, the matrix-core scan (32 queries per key tile) and
+    the per-query scan give the same scores and block maxima, bit for bit, for
+    all 4,096 queries."""
+    from tests.gpu_inputs import DeviceWorkload
+    cfg = wl.CONFIGS["prefill"]
+    _say("prefill: matrix-core scan vs per-query scan, all queries")
+    dw = DeviceWorkload(cfg, gpu, build_kv=False)
+    s_mfma, b_mfma = fk.fp4kv_index_scores(dw.idx_q[0], dw.w[0], dw.idx_k, dw.q_seq_start, dw.q_pos, cfg.T, cfg.ctx)
+    starts = dw.q_seq_start.repeat(cfg.T)           # one "sequence" per query: the per-query scan
+    s_one, b_one = fk.fp4kv_index_scores(dw.idx_q[0], dw.w[0], dw.idx_k, starts, dw.q_pos, 1, cfg.ctx)
+    torch.cuda.synchronize()
+    vis = (dw.q_pos.to(torch.int64) + 1)
+    cols = torch.arange(cfg.ctx, device=gpu)
+    mask = cols[None, :] < vis[:, None]
+    assert torch.equal(torch.where(mask, s_mfma, 0.0), torch.where(mask, s_one, 0.0))
+    bmask = torch.arange(b_mfma.shape[1], device=gpu)[None, :] < ((vis + 7) // 8)[:, None]
+    assert torch.equal(torch.where(bmask, b_mfma, 0.0), torch.where(bmask, b_one, 0.0))

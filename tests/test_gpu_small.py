@@ -395,3 +395,46 @@ def test_repeatable_bits(fk, gpu):
     a = _indexer_case(fk, gpu, [30000, 7777], 16, 128, 256, 512, seed=21, lo=-1, hi=1)
     b = _indexer_case(fk, gpu, [30000, 7777], 16, 128, 256, 512, seed=21, lo=-1, hi=1)
     assert np.array_equal(a[5], b[5])
+
+
+@pytest.mark.parametrize("P,k", [(64, 96), (64, 40)])
+def test_index_full_many_queries_narrow_selection(fk, gpu, P, k):
+    """300 queries (600 selection workgroups, the instance held to 64 VGPRs so
+    that two share a CU), short ragged contexts with heavy ties, the pool
+    smaller and larger than k: every query's pool and indices against the oracle."""
+    _say(f"index_full 300 queries, narrow selection instance, P={P} k={k}")
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(1, 3000, 300)]
+    _indexer_case(fk, gpu, lengths, 4, 64, P, k, seed=31, lo=-1, hi=1)
+
+
+def test_repeatable_bits_attention_and_append(fk, gpu):
+    """Attention (split partials + combine) and the quantize-append give
+    identical bits when run twice on the same inputs."""
+    _say("determinism: attention and append")
+    lengths = [50000, 3000, 777, 20000]
+    B, k, W, Hq = len(lengths), 512, 128, 64
+    starts = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int64)).to(gpu)
+    total = int(np.sum(lengths))
+    x = normal_bf16(41, "kv", 0, (total, 512), outliers=True, device=gpu)
+    caches = []
+    for _ in range(2):
+        codes = torch.empty((total, 256), dtype=torch.uint8, device=gpu)
+        scales = torch.empty((total, 32), dtype=torch.uint8, device=gpu)
+        fk.fp4kv_quantize_append(x, codes, scales)
+        caches.append((codes, scales))
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0][0], caches[1][0]) and torch.equal(caches[0][1], caches[1][1])
+    rng = np.random.default_rng(41)
+    idx = torch.from_numpy(np.stack([np.sort(rng.choice(n, size=k, replace=False)) for n in lengths])
+                           .astype(np.int32)).to(gpu)
+    nidx = torch.full((B,), k, dtype=torch.int32, device=gpu)
+    qpos = torch.tensor([n - 1 for n in lengths], dtype=torch.int32, device=gpu)
+    q = normal_bf16(41, "q", 0, (B, Hq, 512), outliers=False, device=gpu)
+    wk = normal_bf16(41, "wk", 0, (B, W, 512), outliers=False, device=gpu)
+    wv = normal_bf16(41, "wv", 0, (B, W, 512), outliers=False, device=gpu)
+    assert fk.fp4kv_attn_workspace_bytes(B, Hq, 512, k, W) > 0        # several splits and a combine
+    runs = [fk.fp4kv_sparse_attn_decode(q, caches[0][0], caches[0][1], starts, idx, nidx, wk, wv, qpos,
+                                        1.0 / math.sqrt(512)) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
