@@ -48,8 +48,8 @@ HBM_PEAK_GBPS = 8000.0
 # counter's reading for a plain 1 GiB copy (x1.99994 and x1.0). Valid only for
 # the kernel sources they were taken on: a change to any of them turns the
 # figures into null until the counters are taken again.
-KERNEL_SOURCES = ("api.hip", "attn.hip", "common.h", "kernels.h", "quant.hip", "quant_dev.h", "scan.hip",
-                  "scan_mfma.hip", "select.hip")
+KERNEL_SOURCES = ("api.hip", "attn.hip", "attn_common.h", "common.h", "kernels.h", "quant.hip", "quant_dev.h",
+                  "scan.hip", "scan_mfma.hip", "select.hip")
 STEP_TRAFFIC = {"sources_sha256_16": None, "bytes_per_step": None, "scan_bytes_per_launch": None}
 
 

@@ -144,7 +144,9 @@ fp4kv_status fp4kv_kv_append(int32_t fmt, const void* src, int64_t n_rows, int32
 
 /*
  * Workspace bytes fp4kv_index_full needs for n_q queries whose positions are
- * below max_ctx (token scores and block maxima, fp32).
+ * below max_ctx (token scores and block maxima, fp32). 0 when n_q, max_ctx or
+ * block is not positive, max_ctx exceeds 2^40, or the size does not fit size_t;
+ * the indexer entry points refuse such a request (FP4KV_ERR_SHAPE).
  */
 size_t fp4kv_index_workspace_bytes(int32_t n_q, int64_t max_ctx, int32_t block);
 
@@ -176,7 +178,8 @@ size_t fp4kv_index_workspace_bytes(int32_t n_q, int64_t max_ctx, int32_t block);
  *               negative position sees no token (empty pool and selection);
  *               rows at or past total_rows are treated as not visible.
  *   H, D        H in {4, 8, 16}; D in {64, 128}.
- *   max_ctx     host bound: every q_pos < max_ctx (sizes the grid).
+ *   max_ctx     host bound: every q_pos < max_ctx (sizes the grid); in
+ *               [1, 2^40] for every indexer entry point.
  *   block       tokens per block; must be 8.
  *   P, k        pool blocks and kept tokens; 1 <= P, 1 <= k <= P*block,
  *               P*block <= 16384.

@@ -41,6 +41,28 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int64_t nblk_of(int64_t max_ctx, int block) { return (max_ctx + block - 1) / block; }
 
+// Largest max_ctx the indexer entry points accept (keeps every size and index
+// product in range).
+constexpr int64_t kMaxCtx = int64_t(1) << 40;
+
+// Index workspace bytes (scores, then block maxima), or 0 when the size does
+// not fit size_t.
+size_t index_ws_bytes(int32_t n_q, int64_t max_ctx, int32_t block) {
+  size_t scores = 0, bmax = 0, total = 0;
+  if (__builtin_mul_overflow((size_t)n_q, (size_t)max_ctx, &scores) ||
+      __builtin_mul_overflow(scores, sizeof(float), &scores) || scores > SIZE_MAX - kAlign)
+    return 0;
+  bmax = (size_t)n_q * (size_t)nblk_of(max_ctx, block) * sizeof(float);   // no larger than scores
+  if (__builtin_add_overflow(align_up(scores), align_up(bmax), &total)) return 0;
+  return total;
+}
+
+fp4kv_status check_max_ctx(const char* fn, int64_t max_ctx) {
+  if (max_ctx < 1 || max_ctx > kMaxCtx)
+    return fail(FP4KV_ERR_SHAPE, "%s: max_ctx=%lld must be in [1, 2^40]", fn, (long long)max_ctx);
+  return FP4KV_OK;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -113,9 +135,9 @@ static fp4kv_status check_append(const char* fn, int32_t fmt, const void* src, i
     return fail(FP4KV_ERR_NULL, "%s: src, codes and (except for FP8) scales must be non-NULL", fn);
   if (C <= 0 || C % 32 != 0) return fail(FP4KV_ERR_SHAPE, "%s: C=%d must be a positive multiple of 32", fn, C);
   if (n_rows < 0 || cap_rows < 0) return fail(FP4KV_ERR_SHAPE, "%s: n_rows and cap_rows must be >= 0", fn);
-  if (!dst_rows && (dst_start < 0 || dst_start + n_rows > cap_rows))
-    return fail(FP4KV_ERR_SHAPE, "%s: rows [%lld, %lld) outside the cache of %lld rows", fn, (long long)dst_start,
-                (long long)(dst_start + n_rows), (long long)cap_rows);
+  if (!dst_rows && (dst_start < 0 || dst_start > cap_rows || n_rows > cap_rows - dst_start))
+    return fail(FP4KV_ERR_SHAPE, "%s: %lld rows from row %lld do not fit the cache of %lld rows", fn,
+                (long long)n_rows, (long long)dst_start, (long long)cap_rows);
   if (!aligned16(src) || (reinterpret_cast<uintptr_t>(codes) & 7u))
     return fail(FP4KV_ERR_SHAPE, "%s: src must be 16-byte and codes 8-byte aligned", fn);
   return FP4KV_OK;
@@ -141,14 +163,13 @@ fp4kv_status fp4kv_quantize_append(const void* src, int64_t n_rows, int32_t C, c
 }
 
 size_t fp4kv_index_workspace_bytes(int32_t n_q, int64_t max_ctx, int32_t block) {
-  if (n_q <= 0 || max_ctx <= 0 || block <= 0) return 0;
-  return align_up((size_t)n_q * max_ctx * sizeof(float)) +
-         align_up((size_t)n_q * nblk_of(max_ctx, block) * sizeof(float));
+  if (n_q <= 0 || max_ctx <= 0 || max_ctx > kMaxCtx || block <= 0) return 0;
+  return index_ws_bytes(n_q, max_ctx, block);
 }
 
 size_t fp4kv_reindex_workspace_bytes(int32_t n_q, int32_t P, int32_t block) {
   if (n_q <= 0 || P <= 0 || block <= 0) return 0;
-  return align_up((size_t)n_q * P * block * sizeof(float));
+  return align_up((size_t)n_q * (size_t)P * (size_t)block * sizeof(float));   // < 2^95 / 2^31: fits
 }
 
 size_t fp4kv_attn_workspace_bytes(int32_t n_q, int32_t Hq, int32_t C, int32_t k, int32_t W) {
@@ -252,9 +273,11 @@ fp4kv_status fp4kv_index_full(const void* idx_q, const float* w, const void* idx
                                          H, D, block, P, k, idx_out, n_idx);
   if (st != FP4KV_OK) return st;
   if (!pool_out || !n_pool) return fail(FP4KV_ERR_NULL, "index_full: pool_out and n_pool must be non-NULL");
-  if (max_ctx < 1) return fail(FP4KV_ERR_SHAPE, "index_full: max_ctx=%lld must be >= 1", (long long)max_ctx);
+  st = check_max_ctx("index_full", max_ctx);
+  if (st != FP4KV_OK) return st;
   if (n_q == 0) return ok();
   const size_t need = fp4kv_index_workspace_bytes(n_q, max_ctx, block);
+  if (need == 0) return fail(FP4KV_ERR_SHAPE, "index_full: n_q x max_ctx scores do not fit size_t");
   if (!workspace || ws_bytes < need)
     return fail(FP4KV_ERR_WORKSPACE, "index_full: workspace of %zu bytes, %zu required", ws_bytes, need);
   return index_full_into(idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D, max_ctx, block, P, k,
@@ -270,7 +293,8 @@ fp4kv_status fp4kv_index_scores(const void* idx_q, const float* w, const void* i
                                          q_per_seq, H, D, block, 1, 1, &dummy, &dummy);
   if (st != FP4KV_OK) return st;
   if (!scores || !blockmax) return fail(FP4KV_ERR_NULL, "index_scores: scores and blockmax must be non-NULL");
-  if (max_ctx < 1) return fail(FP4KV_ERR_SHAPE, "index_scores: max_ctx=%lld must be >= 1", (long long)max_ctx);
+  st = check_max_ctx("index_scores", max_ctx);
+  if (st != FP4KV_OK) return st;
   if (n_q == 0) return ok();
   return launch_scores(idx_q, w, idx_k, total_rows, seq_start, q_pos, n_q, q_per_seq, H, D, max_ctx, block, scores,
                        blockmax, static_cast<hipStream_t>(stream));
@@ -282,8 +306,10 @@ fp4kv_status fp4kv_index_select(const float* scores, const float* blockmax, int6
                                 int32_t* n_pool, int32_t* idx_out, int32_t* n_idx, void* stream) {
   if (!scores || !blockmax || !seq_start || !q_pos || !pool_out || !n_pool || !idx_out || !n_idx)
     return fail(FP4KV_ERR_NULL, "index_select: a required pointer is NULL");
-  if (n_q < 0 || q_per_seq < 1 || total_rows < 0 || max_ctx < 1)
-    return fail(FP4KV_ERR_SHAPE, "index_select: n_q >= 0, q_per_seq >= 1, total_rows >= 0, max_ctx >= 1 required");
+  if (n_q < 0 || q_per_seq < 1 || total_rows < 0)
+    return fail(FP4KV_ERR_SHAPE, "index_select: n_q >= 0, q_per_seq >= 1 and total_rows >= 0 required");
+  fp4kv_status st = check_max_ctx("index_select", max_ctx);
+  if (st != FP4KV_OK) return st;
   if (block != 8) return fail(FP4KV_ERR_UNSUPPORTED, "index_select: block=%d (only 8 is implemented)", block);
   if (P < 1 || k < 1) return fail(FP4KV_ERR_SHAPE, "index_select: P=%d and k=%d must be >= 1", P, k);
   if ((int64_t)P * block > 16384) return fail(FP4KV_ERR_UNSUPPORTED, "index_select: P*block exceeds 16384");
@@ -305,7 +331,8 @@ fp4kv_status fp4kv_index_scores_append(const void* idx_q, const float* w, const 
                                          block, 1, 1, &dummy, &dummy);
   if (st != FP4KV_OK) return st;
   if (!scores || !blockmax) return fail(FP4KV_ERR_NULL, "%s: scores and blockmax must be non-NULL", fn);
-  if (max_ctx < 1) return fail(FP4KV_ERR_SHAPE, "%s: max_ctx=%lld must be >= 1", fn, (long long)max_ctx);
+  st = check_max_ctx(fn, max_ctx);
+  if (st != FP4KV_OK) return st;
   st = check_append(fn, kv_fmt, kv_src, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows);
   if (st != FP4KV_OK) return st;
   fp4kv::AppendDst dd{};
@@ -333,10 +360,12 @@ fp4kv_status fp4kv_index_full_append(const void* idx_q, const float* w, const vo
                                          block, P, k, idx_out, n_idx);
   if (st != FP4KV_OK) return st;
   if (!pool_out || !n_pool) return fail(FP4KV_ERR_NULL, "%s: pool_out and n_pool must be non-NULL", fn);
-  if (max_ctx < 1) return fail(FP4KV_ERR_SHAPE, "%s: max_ctx=%lld must be >= 1", fn, (long long)max_ctx);
+  st = check_max_ctx(fn, max_ctx);
+  if (st != FP4KV_OK) return st;
   st = check_append(fn, kv_fmt, kv_src, n_rows, C, dst_rows, dst_start, codes, scales, cap_rows);
   if (st != FP4KV_OK) return st;
   const size_t need = n_q > 0 ? fp4kv_index_workspace_bytes(n_q, max_ctx, block) : 0;
+  if (n_q > 0 && need == 0) return fail(FP4KV_ERR_SHAPE, "%s: n_q x max_ctx scores do not fit size_t", fn);
   if (n_q > 0 && (!workspace || ws_bytes < need))
     return fail(FP4KV_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu required", fn, ws_bytes, need);
   fp4kv::AppendDst dd{};
@@ -602,6 +631,7 @@ fp4kv_status fp4kv_index_full_paged(const void* idx_q, const float* w, const voi
     return fail(FP4KV_ERR_SHAPE, "%s: n_q=%d exceeds n_seq*q_per_seq", fn, n_q);
   if (n_q == 0) return ok();
   const size_t need = fp4kv_index_workspace_bytes(n_q, max_ctx, block);
+  if (need == 0) return fail(FP4KV_ERR_SHAPE, "%s: n_q x max_ctx scores do not fit size_t", fn);
   if (!workspace || ws_bytes < need)
     return fail(FP4KV_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu required", fn, ws_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -719,10 +749,11 @@ fp4kv_status fp4kv_index_full_noalloc(const void* idx_q, const float* w, const v
                                          block, P, k, idx_out, n_idx);
   if (st != FP4KV_OK) return st;
   if (!pool_out || !n_pool) return fail(FP4KV_ERR_NULL, "%s: pool_out and n_pool must be non-NULL", fn);
-  if (max_ctx < 1) return fail(FP4KV_ERR_SHAPE, "%s: max_ctx=%lld must be >= 1", fn, (long long)max_ctx);
+  st = check_max_ctx(fn, max_ctx);
+  if (st != FP4KV_OK) return st;
   if (n_q == 0) return ok();
   const size_t need = fp4kv_index_workspace_bytes(n_q, max_ctx, block);
-  if (need > kNoallocScratchBytes)
+  if (need == 0 || need > kNoallocScratchBytes)
     return fail(FP4KV_ERR_WORKSPACE, "%s: n_q=%d x max_ctx=%lld needs %zu bytes of scores, beyond the fixed %zu",
                 fn, n_q, (long long)max_ctx, need, kNoallocScratchBytes);
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -41,12 +41,10 @@
 // tiles, so each lane's eight P values are exactly the eight rows its P^T
 // operand needs. With one split the result is written directly; otherwise
 // (m, l, O) partials go to the workspace and a combine kernel merges them.
-#include "kernels.h"
+#include "attn_common.h"
 
 namespace fp4kv {
 
-constexpr int kAttnC = 512;       // channels (the kernels are written for 512)
-constexpr int kChunk = 32;        // rows per chunk
 constexpr int kItems = (kChunk / 4) * (kAttnC / 8);   // (4-row, 8-channel) items = 512
 
 constexpr int kRowUnits = kChunk * 64;   // a chunk's rows in 16-byte units (64 per row)
@@ -70,18 +68,6 @@ __device__ __forceinline__ int row_swizzle(int row) {
 }
 __device__ __forceinline__ int kbuf_unit(int row, int u) { return row * 64 + (u ^ row_swizzle(row)); }
 
-// Half the value of an E4M3 scale code (sign bit never set): exact in fp32.
-__device__ __forceinline__ float e4m3_half(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  return e ? __uint_as_float(((e + 119u) << 23) | (m << 20)) : (float)m * 0x1p-10f;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  // exact here: dequantised values fit in bf16
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
 // Raw bytes of one item, loaded one chunk ahead of its use. Sparse and
 // window chunks have register slots of their own, so that no slot ever holds
 // both kinds (merging the two would copy registers that are still being
@@ -99,41 +85,6 @@ struct RawWindow {
   uint4 k[4], v[4];   // bf16 keys and values, channels 8c..8c+7 of row r
   uint32_t valid;
 };
-
-struct QueryInfo {
-  int64_t kv_base;    // first main-KV row of the sequence (contiguous storage)
-  int64_t seq;        // sequence of the query (paged storage)
-  int64_t p;          // query position
-  int n_s, n_w;       // sparse rows, window rows
-  int cs, cw;         // chunks of each
-  int64_t win_row0;   // window-buffer row holding the oldest used window row
-  int64_t ring_base;  // window ring: first row of the query's W rows
-};
-
-__device__ __forceinline__ QueryInfo query_info(const AttnArgs& a, int qi) {
-  QueryInfo r;
-  r.kv_base = a.map.block_table ? 0 : (a.seq_start ? a.seq_start[qi] : a.seq_start_scalar);
-  r.seq = a.map.block_table ? qi / a.page_q_per_seq : 0;
-  int64_t p = a.q_pos ? (int64_t)a.q_pos[qi] : (int64_t)a.pos0 + qi;
-  r.p = p;            // negative: the query sees no token
-  int ns = a.n_idx[qi];
-  r.n_s = ns < 0 ? 0 : (ns > a.k ? a.k : ns);
-  if (!a.map.block_table && (r.kv_base < 0 || r.kv_base > a.total_rows)) r.n_s = 0;   // start outside the cache
-  r.n_w = p < 0 ? 0 : (int)min<int64_t>(a.W, p + 1);
-  r.cs = (r.n_s + kChunk - 1) / kChunk;
-  r.cw = (r.n_w + kChunk - 1) / kChunk;
-  r.win_row0 = (int64_t)qi * a.win_stride + (a.W - r.n_w);
-  r.ring_base = (int64_t)qi * a.W;
-  return r;
-}
-
-// Main-KV row of sparse slot j holding position `pos` at storage row `row`
-// (already mapped), or -1 if the slot is not a usable row.
-__device__ __forceinline__ int64_t sparse_row(const AttnArgs& a, const QueryInfo& qi_, int j, int64_t pos,
-                                              int64_t row) {
-  if (j >= qi_.n_s || pos < 0 || pos > qi_.p || row < 0) return -1;
-  return row < a.total_rows ? row : -1;
-}
 
 // Item `item` of a chunk: row group (4 rows) and channel group (8 channels).
 // Row groups are wave-uniform: a wave covers whole rows.
@@ -253,15 +204,6 @@ __device__ __forceinline__ void store_rows(uint4* buf, int rg, int cg, const uin
   for (int r = 0; r < 4; ++r) buf[kbuf_unit(4 * rg + r, cg)] = make_uint4(d[r][0], d[r][1], d[r][2], d[r][3]);
 }
 
-// bf16 pair (lo, hi) of two E4M3FN codes, exact: a normal code's fields move
-// into an fp32, a subnormal one (m * 2^-9) is formed by a product. (The NaN
-// codes 0x7F and 0xFF are never written by the append and decode as 480.)
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
-}
-
 template <int NHG, int FMT>
 __device__ __forceinline__ void commit_sparse(AttnShared<NHG>& sh, const RawSparse (&raw)[kItems / (128 * NHG)]) {
   constexpr int PER = kItems / (128 * NHG);
@@ -272,44 +214,7 @@ __device__ __forceinline__ void commit_sparse(AttnShared<NHG>& sh, const RawSpar
     const uint32_t valid = raw[it].valid;
     if (cg == 0) sh.vb[rg] = valid;
     uint32_t d[4][4];
-    if constexpr (FMT == kKvFp8) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool real = (valid >> r) & 1u;
-        const uint32_t lo = real ? raw[it].code[r] : 0u, hi = real ? raw[it].scale[r] : 0u;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          d[r][j] = pack_bf16x2(e4m3_to_f32((lo >> (16 * j)) & 0xFFu), e4m3_to_f32((lo >> (16 * j + 8)) & 0xFFu));
-          d[r][2 + j] = pack_bf16x2(e4m3_to_f32((hi >> (16 * j)) & 0xFFu), e4m3_to_f32((hi >> (16 * j + 8)) & 0xFFu));
-        }
-      }
-    } else {
-      // twice the E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 as bytes
-      constexpr uint32_t lut_lo = 0x03020100u, lut_hi = 0x0C080604u;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool real = (valid >> r) & 1u;
-        const uint32_t code = real ? raw[it].code[r] : 0u;
-        float sh2;   // half the block scale (the table holds twice the magnitudes)
-        if constexpr (FMT == kKvMxfp4) {
-          const uint32_t sc = (raw[it].scale[r] >> (8 * ((cg >> 2) & 3))) & 0xFFu;
-          sh2 = real ? __builtin_ldexpf(1.0f, (int)sc - 128) : 0.0f;   // 2^(sc - 127) / 2, exact
-        } else {
-          sh2 = e4m3_half(real ? (raw[it].scale[r] >> (8 * ((cg >> 1) & 3))) & 0xFFu : 0u);
-        }
-        const uint32_t me = __builtin_amdgcn_perm(lut_hi, lut_lo, code & 0x07070707u);         // even channels
-        const uint32_t mo = __builtin_amdgcn_perm(lut_hi, lut_lo, (code >> 4) & 0x07070707u);  // odd channels
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float f0 = (float)((me >> (8 * j)) & 0xFFu) * sh2;
-          float f1 = (float)((mo >> (8 * j)) & 0xFFu) * sh2;
-          // sign bits of nibbles 2j (bit 8j+3) and 2j+1 (bit 8j+7)
-          f0 = __uint_as_float(__float_as_uint(f0) | ((code << (28 - 8 * j)) & 0x80000000u));
-          f1 = __uint_as_float(__float_as_uint(f1) | ((code << (24 - 8 * j)) & 0x80000000u));
-          d[r][j] = pack_bf16x2(f0, f1);
-        }
-      }
-    }
+    dequant_item<FMT>(raw[it].code, raw[it].scale, valid, cg, d);
     store_rows(sh.kbuf, rg, cg, d);
   }
 }
@@ -598,9 +503,9 @@ hipError_t launch_attn(AttnArgs a, void* ws, hipStream_t stream) {
     a.part_o = static_cast<float*>(ws);
     a.part_ml = a.part_o + (size_t)a.nq * a.n_split * a.Hq * kAttnC;
   }
+  if (a.kv_fmt < kKvFp4 || a.kv_fmt > kKvFp8) return hipErrorInvalidValue;
   const int nhg = plan.nhg;
   dim3 grid((uint32_t)a.nq, (uint32_t)a.n_split, (uint32_t)plan.hb);
-  if (a.kv_fmt < kKvFp4 || a.kv_fmt > kKvFp8) return hipErrorInvalidValue;
   const bool paged = a.map.block_table != nullptr;
 #define FP4KV_ATTN_CASE(NH, FM)                                                                  \
   if (nhg == NH && a.kv_fmt == FM) {                                                             \

@@ -65,3 +65,11 @@ def test_attention_bytes_count_inputs_and_outputs_once():
 def test_kernel_sources_hash_is_stable():
     assert len(bench.sources_hash()) == 16
     assert bench.sources_hash() == bench.sources_hash()
+
+
+def test_kernel_sources_cover_every_source_file():
+    # the hash that dates the stored counter traffic must change with any kernel source
+    import os
+    csrc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "sparse_indexer_fp4_amd", "csrc")
+    on_disk = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    assert sorted(bench.KERNEL_SOURCES) == on_disk
