@@ -156,16 +156,19 @@ __device__ __forceinline__ void load_sparse(const AttnArgs& a, const QueryInfo& 
     for (int r = 0; r < 4; ++r) {
       const int j = c * kChunk + 4 * rg + r;
       const int64_t row = chunk_row<NHG, PAGED>(a, Q, qi, m, j, it, r, lp);
-      const int64_t rr = row < 0 ? 0 : row;
+      // a slot without a row reads the query instead (always present; zeroed at commit)
+      const uint8_t* stand_in = reinterpret_cast<const uint8_t*>(a.q);
       if constexpr (FMT == kKvFp8) {
-        const uint2 v = *reinterpret_cast<const uint2*>(a.codes + rr * kAttnC + 8 * cg);
+        const uint8_t* cb = row < 0 ? stand_in : a.codes + row * kAttnC;
+        const uint2 v = *reinterpret_cast<const uint2*>(cb + 8 * cg);
         raw[it].code[r] = v.x;
         raw[it].scale[r] = v.y;
       } else {
         constexpr int kGroupShift = FMT == kKvMxfp4 ? 2 : 1;     // items (8 channels) per scale byte: 4 or 2
-        raw[it].code[r] = *reinterpret_cast<const uint32_t*>(a.codes + rr * (kAttnC / 2) + 4 * cg);
-        raw[it].scale[r] = *reinterpret_cast<const uint32_t*>(
-            a.scales + rr * (kAttnC / (8 << kGroupShift)) + 4 * (cg >> (kGroupShift + 2)));
+        const uint8_t* cb = row < 0 ? stand_in : a.codes + row * (kAttnC / 2);
+        const uint8_t* sb = row < 0 ? stand_in : a.scales + row * (kAttnC / (8 << kGroupShift));
+        raw[it].code[r] = *reinterpret_cast<const uint32_t*>(cb + 4 * cg);
+        raw[it].scale[r] = *reinterpret_cast<const uint32_t*>(sb + 4 * (cg >> (kGroupShift + 2)));
       }
       bits |= (uint32_t)(row >= 0) << r;
     }
@@ -187,9 +190,7 @@ __device__ __forceinline__ void load_window(const AttnArgs& a, const QueryInfo& 
       const int wr = (c - Q.cs) * kChunk + 4 * rg + r;
       const bool ok = wr < Q.n_w;
       bits |= (uint32_t)ok << r;
-      // a ring keeps position t in slot t mod W of the query's W rows
-      const int64_t row = a.ring ? Q.ring_base + (Q.p - Q.n_w + 1 + (ok ? wr : 0)) % a.W
-                                 : Q.win_row0 + (ok ? wr : 0);
+      const int64_t row = window_row(a, Q, ok ? wr : 0);
       raw[it].k[r] = *reinterpret_cast<const uint4*>(a.swa_k + row * kAttnC + 8 * cg);
       raw[it].v[r] = *reinterpret_cast<const uint4*>(a.swa_v + row * kAttnC + 8 * cg);
     }
