@@ -50,7 +50,11 @@ HBM_PEAK_GBPS = 8000.0
 # figures into null until the counters are taken again.
 KERNEL_SOURCES = ("api.hip", "attn.hip", "attn_common.h", "common.h", "kernels.h", "quant.hip", "quant_dev.h",
                   "scan.hip", "scan_mfma.hip", "select.hip")
-STEP_TRAFFIC = {"sources_sha256_16": None, "bytes_per_step": None, "scan_bytes_per_launch": None}
+# HBM bytes from rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated against a copy of known size:
+# one decode128k step (scan carrying the append, selection, attention, combine) and one scan
+# launch as the breakdown pass times it. Valid only for the kernel sources they were taken on.
+STEP_TRAFFIC = {"sources_sha256_16": "a3602dfd877cc4cb", "bytes_per_step": 1191161390,
+                "scan_bytes_per_launch": 1095361661}
 
 
 def log(msg):
