@@ -110,3 +110,24 @@ def test_index_full_append_matrix_core_scan(fk, gpu):
     for name, a, b in zip(("pool", "n_pool", "idx", "n_idx"), ref, got):
         assert torch.equal(a, b), name
     assert torch.equal(ref_c, got_c) and torch.equal(ref_s, got_s)
+
+
+@pytest.mark.parametrize("fmt", [0, 2])
+def test_index_scores_append_single_query_grid(fk, gpu, fmt):
+    """One query: the scan takes its 2-D grid (no work list) with the append rows as
+    a second grid row."""
+    _say(f"index_scores_append: one query, 2-D grid, fmt={fmt}")
+    q, w, kk, starts, qpos, max_ctx = _indexer(gpu, [50001], 16, 128, seed=89 + fmt)
+    x = normal_bf16(90, "kv", fmt, (300, 512), outliers=True).to(gpu)
+    ref_c, ref_s = _cache(fk, gpu, fmt, 2000)
+    fk.fp4kv_kv_append(fmt, x, ref_c, ref_s, dst_start=1700)
+    rs, rb = fk.fp4kv_index_scores(q, w, kk, starts, qpos, 1, max_ctx)
+    got_c, got_s = _cache(fk, gpu, fmt, 2000)
+    gs, gb = fk.fp4kv_index_scores_append(q, w, kk, starts, qpos, 1, max_ctx, x, got_c, got_s, dst_start=1700,
+                                          kv_fmt=fmt)
+    torch.cuda.synchronize()
+    assert torch.equal(rs[0, :50001], gs[0, :50001])
+    assert torch.equal(rb[0, :(50001 + 7) // 8], gb[0, :(50001 + 7) // 8])
+    assert torch.equal(ref_c, got_c)
+    if ref_s is not None:
+        assert torch.equal(ref_s, got_s)
