@@ -95,16 +95,33 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a, MfmaSc
     // ---------------- copy wave
     const char* kseq = reinterpret_cast<const char*>(a.idx_k + base * D);
     const int64_t last = maxv - 1;            // rows past every query's visibility are never read back
+    // Byte offset within a tile of this lane's 16-byte chunk of each copy
+    // instruction: the same for every tile, so a whole tile's loads are a
+    // uniform tile base plus these (only the last, partial tile clamps rows).
+    uint32_t off[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int slot = i * 64 + lane, tok = slot / NCH, c = (slot % NCH) ^ (tok % NCH);
+      off[i] = (uint32_t)(tok * (D * 2) + c * 16);
+    }
     auto issue = [&](int st) {
       const int64_t t0 = r0 + (int64_t)st * kMTile;
       uint4* dst = ring[st % kMRing];
+      if (t0 + kMTile - 1 <= last) {
+        const char* tb = kseq + t0 * (D * 2);
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int slot = i * 64 + lane, tok = slot / NCH, c = (slot % NCH) ^ (tok % NCH);
-        int64_t t = t0 + tok;
-        t = t > last ? last : t;
-        __builtin_amdgcn_global_load_lds((const void*)(kseq + t * (D * 2) + c * 16),
-                                         (__attribute__((address_space(3))) void*)&dst[i * 64], 16, 0, 0);
+        for (int i = 0; i < NL; ++i)
+          __builtin_amdgcn_global_load_lds((const void*)(tb + off[i]),
+                                           (__attribute__((address_space(3))) void*)&dst[i * 64], 16, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const int slot = i * 64 + lane, tok = slot / NCH, c = (slot % NCH) ^ (tok % NCH);
+          int64_t t = t0 + tok;
+          t = t > last ? last : t;
+          __builtin_amdgcn_global_load_lds((const void*)(kseq + t * (D * 2) + c * 16),
+                                           (__attribute__((address_space(3))) void*)&dst[i * 64], 16, 0, 0);
+        }
       }
     };
     issue(0);
