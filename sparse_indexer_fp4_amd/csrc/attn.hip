@@ -28,7 +28,7 @@
 // n_split-th 32-row chunk, its first window chunk first. Each chunk is
 // dequantised once into LDS by the whole workgroup, one (4 rows x 8 channels)
 // item per thread: the codes of a row are read as one coalesced 256-byte line
-// per wave and E2M1 magnitudes come from a byte table (v_perm). Rows are stored
+// per wave and decoded by the hardware FP4 and FP8 converters. Rows are stored
 // row-major only, with an XOR swizzle of the 16-byte units that keeps the S
 // reads, the P V reads and the commit writes free of bank conflicts; the V^T
 // operand of O^T = V^T P^T is read from the same rows with the LDS transposing
@@ -37,7 +37,8 @@
 // positions a split needs are read with one vector load at the start; the raw
 // bytes of the next sparse chunk are loaded into registers while the current
 // one is computed and are not touched until it is committed, so the loads stay
-// in flight. Chunk rows 2j and 2j+1 are the j-th rows of the two 16-row MFMA
+// in flight. Each step issues all of its LDS reads of K (and most of V) before
+// the products that use them, so the products wait for the first read only. Chunk rows 2j and 2j+1 are the j-th rows of the two 16-row MFMA
 // tiles, so each lane's eight P values are exactly the eight rows its P^T
 // operand needs. With one split the result is written directly; otherwise
 // (m, l, O) partials go to the workspace and a combine kernel merges them.
@@ -205,6 +206,15 @@ __device__ __forceinline__ void store_rows(uint4* buf, int rg, int cg, const uin
   for (int r = 0; r < 4; ++r) buf[kbuf_unit(4 * rg + r, cg)] = make_uint4(d[r][0], d[r][1], d[r][2], d[r][3]);
 }
 
+// Maximum over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48)
+// by the two lane-swap permutes: register-to-register, no LDS round trip.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 template <int NHG, int FMT>
 __device__ __forceinline__ void commit_sparse(AttnShared<NHG>& sh, const RawSparse (&raw)[kItems / (128 * NHG)]) {
   constexpr int PER = kItems / (128 * NHG);
@@ -243,6 +253,21 @@ __device__ __forceinline__ void commit_window(AttnShared<NHG>& sh, const RawWind
     }
     store_rows(sh.vbuf, rg, cg, d);
   }
+}
+
+// V^T operand of channel tile t (channels 256hc + 16t .. +15, chunk rows
+// 8g .. 8g+7) by two transposing reads: lane 4a+b of a 16-lane group gets
+// element b of the 8-byte words addressed by lanes a, 4+a, 8+a, 12+a, so lane
+// i addresses row 8g + 4h + i/4, channels 16t + 4(i%4) .. +3 (h = 0, 1 for
+// the two reads).
+__device__ __forceinline__ v8bf read_vt(const uint4* vrows, int hc, int g, int hcol, int t) {
+  const int tr_row = 8 * g + (hcol >> 2), tr_half = 8 * (hcol & 1);
+  const int u = 32 * hc + 2 * t + ((hcol & 3) >> 1);
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(reinterpret_cast<const char*>(vrows + kbuf_unit(tr_row, u)) + tr_half));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(reinterpret_cast<const char*>(vrows + kbuf_unit(tr_row + 4, u)) + tr_half));
+  return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Workgroup = (query, split): two waves per group of 16 heads, each owning half
@@ -334,15 +359,32 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
     if (step >= w0 && i + 1 < nS) load_sparse<NHG, FMT, PAGED>(a, Q, qi, split + (i + 1) * ns_, i + 1, lp, rs);
 
     // partial S^T over this channel half: A = even rows (tile 0) / odd rows (tile 1), B = Q^T
+    // (all 16 K reads are issued before the first product, so that the
+    // products wait for the first read only)
     v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    uint4 kr0[8], kr1[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const uint4 k0 = sh.kbuf[kbuf_unit(2 * hcol, 32 * hc + 4 * kk + g)];
-      const uint4 k1 = sh.kbuf[kbuf_unit(2 * hcol + 1, 32 * hc + 4 * kk + g)];
-      const v8bf b = __builtin_bit_cast(v8bf, qv[kk]);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, k0), b, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, k1), b, s1, 0, 0, 0);
+      kr0[kk] = sh.kbuf[kbuf_unit(2 * hcol, 32 * hc + 4 * kk + g)];
+      kr1[kk] = sh.kbuf[kbuf_unit(2 * hcol + 1, 32 * hc + 4 * kk + g)];
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const v8bf b = __builtin_bit_cast(v8bf, qv[kk]);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kr0[kk]), b, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kr1[kk]), b, s1, 0, 0, 0);
+    }
+    // V^T operands of the 16 channel tiles. The first kEarly are read now, so
+    // that the reads overlap the S products, the exchange and the softmax; the
+    // rest (paged storage keeps more registers live) just before the products
+    // that use them.
+    constexpr int kEarly = PAGED ? 8 : 16;
+    const uint4* vrows = window ? sh.vbuf : sh.kbuf;    // values: the latent rows themselves, or the window's
+    v8bf vt[16];
+#pragma unroll
+    for (int t = 0; t < kEarly; ++t) vt[t] = read_vt(vrows, hc, g, hcol, t);
+    __builtin_amdgcn_sched_barrier(0);
     {
       float4* mine = reinterpret_cast<float4*>(&sh.sp[hg][hc][lane][0]);
       mine[0] = make_float4(s0[0], s0[1], s0[2], s0[3]);
@@ -368,13 +410,12 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
     float cm = x[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) cm = fmaxf(cm, x[i]);
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    cm = max_over_rows(cm);
     if (cm == -__builtin_inff() && m_use == -__builtin_inff()) continue;   // nothing usable yet (per head)
     // move the reference maximum only when this chunk exceeds it by more than 2^8
     const bool move = cm > m_use + 8.0f;
     if (__builtin_amdgcn_ballot_w64(move)) {
-      const float corr = move ? exp2f(m_use - cm) : 1.0f;
+      const float corr = move ? __builtin_amdgcn_exp2f(m_use - cm) : 1.0f;
       if (move) m_use = cm;
       l_run *= corr;
 #pragma unroll
@@ -382,7 +423,7 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
     }
     float p[8], psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { p[i] = exp2f(x[i] - m_use); psum += p[i]; }
+    for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - m_use); psum += p[i]; }
     l_run += psum;
     v8bf phi, plo;
 #pragma unroll
@@ -391,22 +432,12 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
       phi[i] = h;
       plo[i] = (__bf16)(p[i] - (float)h);
     }
-    uint4* vrows = window ? sh.vbuf : sh.kbuf;    // values: the latent rows themselves, or the window's
-    const int tr_row = 8 * g + (hcol >> 2), tr_half = 8 * (hcol & 1);
+#pragma unroll
+    for (int t = kEarly; t < 16; ++t) vt[t] = read_vt(vrows, hc, g, hcol, t);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      // V^T operand (channels ch0 + hcol, rows 8g .. 8g+7) by two transposing
-      // reads: lane 4a+b of a 16-lane group gets element b of the 8-byte words
-      // addressed by lanes a, 4+a, 8+a, 12+a, so lane i addresses row
-      // 8g + 4h + i/4, channels ch0 + 4(i%4) .. +3.
-      const int u = 32 * hc + 2 * t + ((hcol & 3) >> 1);
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(reinterpret_cast<char*>(vrows + kbuf_unit(tr_row, u)) + tr_half));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(reinterpret_cast<char*>(vrows + kbuf_unit(tr_row + 4, u)) + tr_half));
-      const v8s vtile = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, vtile), phi, o[t], 0, 0, 0);
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, vtile), plo, o[t], 0, 0, 0);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[t], phi, o[t], 0, 0, 0);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[t], plo, o[t], 0, 0, 0);
     }
   }
 

@@ -9,12 +9,6 @@ namespace fp4kv {
 constexpr int kAttnC = 512;       // channels (the kernels are written for 512)
 constexpr int kChunk = 32;        // rows per chunk
 
-// Half the value of an E4M3 scale code (sign bit never set): exact in fp32.
-__device__ __forceinline__ float e4m3_half(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  return e ? __uint_as_float(((e + 119u) << 23) | (m << 20)) : (float)m * 0x1p-10f;
-}
-
 // Two floats as a bf16 pair (lo in the low half), rounded to nearest even;
 // exact for dequantised values, which fit in bf16.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -23,13 +17,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));   // one v_cvt_pk_bf16_f32
 }
 
-// bf16 pair (lo, hi) of two E4M3FN codes, exact: a normal code's fields move
-// into an fp32, a subnormal one (m * 2^-9) is formed by a product. (The NaN
-// codes 0x7F and 0xFF are never written by the append and decode as 480.)
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
+// Channels 2j and 2j+1 (the low and high nibble of byte j of c) as E2M1 values
+// times s, as a bf16 pair. The hardware converter decodes the two nibbles
+// exactly into fp32; the product with an E4M3 or E8M0 scale has at most 6
+// significant bits, so it and its bf16 rounding are exact. (The converter's
+// own scale operand is not used: it applies only the exponent of its scale.)
+template <int J>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t c, float s) {
+  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, J);
+  return pack_bf16x2(v[0] * s, v[1] * s);
 }
 
 // Eight channels of one row as four bf16 pairs, dequantised exactly: E2M1 x
@@ -37,39 +33,25 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 // MXFP4: cw holds the eight E2M1 nibbles (channel 2i in the low nibble of byte
 // i) and sc the row's scale code for them in its low byte. FP8: cw and sc hold
 // the E4M3 codes of channels 0-3 and 4-7. A row that is not real comes out as
-// zeros.
+// zeros. E4M3 codes go through the hardware E4M3FN converter (exact; the NaN
+// codes 0x7F and 0xFF, which the append never writes, give NaN).
 template <int FMT>
 __device__ __forceinline__ uint4 dequant8(uint32_t cw, uint32_t sc, bool real) {
-  uint32_t d[4];
   if constexpr (FMT == kKvFp8) {
     const uint32_t lo = real ? cw : 0u, hi = real ? sc : 0u;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      d[j] = pack_bf16x2(e4m3_to_f32((lo >> (16 * j)) & 0xFFu), e4m3_to_f32((lo >> (16 * j + 8)) & 0xFFu));
-      d[2 + j] = pack_bf16x2(e4m3_to_f32((hi >> (16 * j)) & 0xFFu), e4m3_to_f32((hi >> (16 * j + 8)) & 0xFFu));
-    }
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), e = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+    return make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
+                      pack_bf16x2(e[0], e[1]));
   } else {
-    // twice the E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 as bytes
-    constexpr uint32_t lut_lo = 0x03020100u, lut_hi = 0x0C080604u;
     const uint32_t c = real ? cw : 0u;
-    float sh2;   // half the block scale (the table holds twice the magnitudes)
+    float s;   // the block scale
     if constexpr (FMT == kKvMxfp4)
-      sh2 = real ? __builtin_ldexpf(1.0f, (int)(sc & 0xFFu) - 128) : 0.0f;   // 2^(sc - 127) / 2, exact
+      s = real ? __builtin_ldexpf(1.0f, (int)(sc & 0xFFu) - 127) : 0.0f;   // 2^(sc - 127), exact
     else
-      sh2 = e4m3_half(real ? sc & 0xFFu : 0u);
-    const uint32_t me = __builtin_amdgcn_perm(lut_hi, lut_lo, c & 0x07070707u);         // even channels
-    const uint32_t mo = __builtin_amdgcn_perm(lut_hi, lut_lo, (c >> 4) & 0x07070707u);  // odd channels
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float f0 = (float)((me >> (8 * j)) & 0xFFu) * sh2;
-      float f1 = (float)((mo >> (8 * j)) & 0xFFu) * sh2;
-      // sign bits of nibbles 2j (bit 8j+3) and 2j+1 (bit 8j+7)
-      f0 = __uint_as_float(__float_as_uint(f0) | ((c << (28 - 8 * j)) & 0x80000000u));
-      f1 = __uint_as_float(__float_as_uint(f1) | ((c << (24 - 8 * j)) & 0x80000000u));
-      d[j] = pack_bf16x2(f0, f1);
-    }
+      s = real ? __builtin_amdgcn_cvt_f32_fp8(sc, 0) : 0.0f;
+    return make_uint4(e2m1_pair<0>(c, s), e2m1_pair<1>(c, s), e2m1_pair<2>(c, s), e2m1_pair<3>(c, s));
   }
-  return make_uint4(d[0], d[1], d[2], d[3]);
 }
 
 // Dequantised bf16 pairs d[r][0..3] (channels 8cg..8cg+7 of rows r = 0..3 of an
