@@ -92,52 +92,53 @@ struct RawWindow {
 __device__ __forceinline__ int item_rows(int item) { return __builtin_amdgcn_readfirstlane(item >> 6); }
 
 // The selected positions a wave needs are read with one vector load when the
-// workgroup starts: lane l holds the position of row 4*rg + (l & 3) of the
+// workgroup starts: lane l takes the position of row 4*rg + (l & 3) of the
 // m-th chunk of this split, where m = l / (4 PER) and rg is the row group of the
-// wave's item (l / 4) % PER. With paged storage the lane also maps it through
-// the block table (one more vector load) and holds the physical row. Chunks
-// past the 16/PER covered read and map their positions directly.
+// wave's item (l / 4) % PER. The lane checks it once (slot within n_s, position
+// within the query's causal range, row inside the cache; with paged storage it
+// maps it through the block table first) and keeps the addresses of the row's
+// codes and scale bytes, or of the stand-in (the query, always present) for a
+// slot that is not a usable row; a ballot keeps which slots are rows. In the
+// loop a row then costs four lane reads. Chunks past the 16/PER covered this
+// way check their rows where they are loaded.
 struct LanePos {
-  int pos;
-  uint32_t row_lo, row_hi;     // paged: physical row
+  uint32_t c_lo, c_hi;     // codes of the slot's row (or the stand-in)
+  uint32_t s_lo, s_hi;     // scale bytes of the slot's row (or the stand-in)
+  uint64_t real;           // wave-uniform: bit l set when lane l's slot is a row
 };
 
-template <int NHG, bool PAGED>
-__device__ __forceinline__ LanePos idx_lane_load(const AttnArgs& a, int qi, int split, int lane) {
+template <int FMT>
+__device__ __forceinline__ constexpr int64_t code_row_bytes() { return FMT == kKvFp8 ? kAttnC : kAttnC / 2; }
+template <int FMT>
+__device__ __forceinline__ constexpr int64_t scale_row_bytes() { return FMT == kKvMxfp4 ? kAttnC / 32 : kAttnC / 16; }
+
+template <int NHG, int FMT, bool PAGED>
+__device__ __forceinline__ LanePos idx_lane_load(const AttnArgs& a, const QueryInfo& Q, int qi, int split, int lane) {
   constexpr int PER = kItems / (128 * NHG);
   const int m = lane / (4 * PER), it = (lane / 4) % PER, r = lane & 3;
   const int rg = (int)(threadIdx.x >> 6) + it * 2 * NHG;   // item_rows of item threadIdx.x + it * 128 * NHG
   const int j = (split + m * a.n_split) * kChunk + 4 * rg + r;
+  const int64_t pos = j < a.k ? a.idx[(int64_t)qi * a.k + j] : -1;
+  const int64_t row = sparse_row(a, Q, j, pos, PAGED ? paged_row(a.map, Q.seq, pos) : Q.kv_base + pos);
+  const uint8_t* stand_in = reinterpret_cast<const uint8_t*>(a.q);
+  const uint64_t cb = reinterpret_cast<uint64_t>(row < 0 ? stand_in : a.codes + row * code_row_bytes<FMT>());
+  const uint64_t sb = FMT == kKvFp8 ? cb   // (FP8 rows have no scale bytes)
+                                    : reinterpret_cast<uint64_t>(row < 0 ? stand_in : a.scales + row * scale_row_bytes<FMT>());
   LanePos lp;
-  lp.pos = j < a.k ? a.idx[(int64_t)qi * a.k + j] : -1;
-  lp.row_lo = lp.row_hi = 0;
-  if constexpr (PAGED) {
-    const int64_t row = paged_row(a.map, qi / a.page_q_per_seq, lp.pos);
-    lp.row_lo = (uint32_t)row;
-    lp.row_hi = (uint32_t)((uint64_t)row >> 32);
-  }
+  lp.c_lo = (uint32_t)cb;
+  lp.c_hi = (uint32_t)(cb >> 32);
+  lp.s_lo = (uint32_t)sb;
+  lp.s_hi = (uint32_t)(sb >> 32);
+  lp.real = __builtin_amdgcn_ballot_w64(row >= 0);
   return lp;
 }
 
-// Storage row of sparse slot j (the m-th chunk of the split, item it, row r),
-// or -1 if the slot is not a usable row.
-template <int NHG, bool PAGED>
-__device__ __forceinline__ int64_t chunk_row(const AttnArgs& a, const QueryInfo& Q, int qi, int m, int j, int it,
-                                             int r, const LanePos& lp) {
-  constexpr int PER = kItems / (128 * NHG);
-  int64_t pos, row;
-  if (m < 16 / PER) {
-    const int l = (m * PER + it) * 4 + r;
-    pos = __builtin_amdgcn_readlane(lp.pos, l);
-    if constexpr (PAGED)
-      row = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lp.row_hi, l) << 32) |
-                      (uint32_t)__builtin_amdgcn_readlane((int)lp.row_lo, l));
-  } else {
-    pos = j < a.k ? a.idx[(int64_t)qi * a.k + j] : -1;
-    if constexpr (PAGED) row = paged_row(a.map, Q.seq, pos);
-  }
-  if constexpr (!PAGED) row = Q.kv_base + pos;
-  return sparse_row(a, Q, j, pos, row);
+// Storage row of sparse slot j of a chunk past the preloaded ones, or -1 if
+// the slot is not a usable row.
+template <bool PAGED>
+__device__ __forceinline__ int64_t late_chunk_row(const AttnArgs& a, const QueryInfo& Q, int qi, int j) {
+  const int64_t pos = j < a.k ? a.idx[(int64_t)qi * a.k + j] : -1;
+  return sparse_row(a, Q, j, pos, PAGED ? paged_row(a.map, Q.seq, pos) : Q.kv_base + pos);
 }
 
 // Issue the loads of chunk c, the m-th chunk of this split: FP4 codes and
@@ -155,23 +156,36 @@ __device__ __forceinline__ void load_sparse(const AttnArgs& a, const QueryInfo& 
     uint32_t bits = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int j = c * kChunk + 4 * rg + r;
-      const int64_t row = chunk_row<NHG, PAGED>(a, Q, qi, m, j, it, r, lp);
-      // a slot without a row reads the query instead (always present; zeroed at commit)
-      const uint8_t* stand_in = reinterpret_cast<const uint8_t*>(a.q);
+      // the addresses of the row's code and scale bytes, or of the stand-in
+      // for a slot without a row (zeroed at commit)
+      uint64_t cb, sb;
+      bool real;
+      if (m < 16 / PER) {
+        const int l = (m * PER + it) * 4 + r;
+        cb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lp.c_hi, l) << 32) |
+             (uint32_t)__builtin_amdgcn_readlane((int)lp.c_lo, l);
+        sb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lp.s_hi, l) << 32) |
+             (uint32_t)__builtin_amdgcn_readlane((int)lp.s_lo, l);
+        real = (lp.real >> l) & 1u;
+      } else {
+        const int64_t row = late_chunk_row<PAGED>(a, Q, qi, c * kChunk + 4 * rg + r);
+        const uint8_t* stand_in = reinterpret_cast<const uint8_t*>(a.q);
+        real = row >= 0;
+        cb = reinterpret_cast<uint64_t>(real ? a.codes + row * code_row_bytes<FMT>() : stand_in);
+        sb = FMT == kKvFp8 ? cb : reinterpret_cast<uint64_t>(real ? a.scales + row * scale_row_bytes<FMT>() : stand_in);
+      }
+      // (global pointers: the addresses are device memory, so the loads are
+      // global rather than flat loads)
+      typedef const __attribute__((address_space(1))) uint32_t* gptr32;
       if constexpr (FMT == kKvFp8) {
-        const uint8_t* cb = row < 0 ? stand_in : a.codes + row * kAttnC;
-        const uint2 v = *reinterpret_cast<const uint2*>(cb + 8 * cg);
-        raw[it].code[r] = v.x;
-        raw[it].scale[r] = v.y;
+        raw[it].code[r] = reinterpret_cast<gptr32>(cb + 8 * cg)[0];
+        raw[it].scale[r] = reinterpret_cast<gptr32>(cb + 8 * cg)[1];
       } else {
         constexpr int kGroupShift = FMT == kKvMxfp4 ? 2 : 1;     // items (8 channels) per scale byte: 4 or 2
-        const uint8_t* cb = row < 0 ? stand_in : a.codes + row * (kAttnC / 2);
-        const uint8_t* sb = row < 0 ? stand_in : a.scales + row * (kAttnC / (8 << kGroupShift));
-        raw[it].code[r] = *reinterpret_cast<const uint32_t*>(cb + 4 * cg);
-        raw[it].scale[r] = *reinterpret_cast<const uint32_t*>(sb + 4 * (cg >> (kGroupShift + 2)));
+        raw[it].code[r] = reinterpret_cast<gptr32>(cb + 4 * cg)[0];
+        raw[it].scale[r] = reinterpret_cast<gptr32>(sb + 4 * (cg >> (kGroupShift + 2)))[0];
       }
-      bits |= (uint32_t)(row >= 0) << r;
+      bits |= (uint32_t)real << r;
     }
     raw[it].valid = bits;
   }
@@ -286,8 +300,8 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   const int hg = wave >> 1, hc = wave & 1;          // head group, channel half
   const int g = lane / 16, hcol = lane % 16;
   const int head = ((int)blockIdx.z * NHG + hg) * 16 + hcol;   // z: this block's group of NHG head groups
-  const LanePos lp = idx_lane_load<NHG, PAGED>(a, qi, split, lane);
   const QueryInfo Q = query_info(a, qi);
+  const LanePos lp = idx_lane_load<NHG, FMT, PAGED>(a, Q, qi, split, lane);
   const int nchunk = Q.cs + Q.cw;
 
   // Q^T operand over this wave's channel half: lane holds Q[head][256hc + 32kk + 8g .. +7]
@@ -379,7 +393,7 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
     // that the reads overlap the S products, the exchange and the softmax; the
     // rest (paged storage keeps more registers live) just before the products
     // that use them.
-    constexpr int kEarly = PAGED ? 8 : 16;
+    constexpr int kEarly = PAGED ? 8 : 14;
     const uint4* vrows = window ? sh.vbuf : sh.kbuf;    // values: the latent rows themselves, or the window's
     v8bf vt[16];
 #pragma unroll
