@@ -54,7 +54,7 @@ template <int NHG>
 struct AttnShared {
   uint4 kbuf[kRowUnits];                 // row-major bf16 keys (= values for sparse rows): 32 KB
   uint4 vbuf[kRowUnits];                 // row-major bf16 values of a window chunk: 32 KB
-  float sp[NHG][2][64][8];               // partial S of each head group's two channel halves
+  float4 sp[NHG][2][2][64];              // partial S of each head group's two channel halves, [tile][lane]
   uint32_t vb[kChunk / 4];               // bit r of word q: chunk row 4q+r is a real row
 };
 
@@ -273,14 +273,20 @@ __device__ __forceinline__ void commit_window(AttnShared<NHG>& sh, const RawWind
 // 8g .. 8g+7) by two transposing reads: lane 4a+b of a 16-lane group gets
 // element b of the 8-byte words addressed by lanes a, 4+a, 8+a, 12+a, so lane
 // i addresses row 8g + 4h + i/4, channels 16t + 4(i%4) .. +3 (h = 0, 1 for
-// the two reads).
-__device__ __forceinline__ v8bf read_vt(const uint4* vrows, int hc, int g, int hcol, int t) {
-  const int tr_row = 8 * g + (hcol >> 2), tr_half = 8 * (hcol & 1);
-  const int u = 32 * hc + 2 * t + ((hcol & 3) >> 1);
+// the two reads). vt_byte gives the byte offset of a lane's word for tile 0;
+// tile t only XORs t into bits 5-8 (its 16-byte unit is 2t above tile 0's,
+// bits 1-4 of the unit index, which the row swizzle leaves alone apart from
+// its own XOR), so read_vt needs one XOR per read.
+__device__ __forceinline__ uint32_t vt_byte(int hc, int hcol, int row) {
+  return (uint32_t)(kbuf_unit(row, 32 * hc + ((hcol & 3) >> 1)) * 16 + 8 * (hcol & 1));
+}
+template <int NHG>
+__device__ __forceinline__ v8bf read_vt(const AttnShared<NHG>& sh, uint32_t lo0, uint32_t hi0, int t) {
+  const char* base = reinterpret_cast<const char*>(&sh);
   const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4s*)(reinterpret_cast<const char*>(vrows + kbuf_unit(tr_row, u)) + tr_half));
+      (__attribute__((address_space(3))) v4s*)(base + (lo0 ^ ((uint32_t)t << 5))));
   const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4s*)(reinterpret_cast<const char*>(vrows + kbuf_unit(tr_row + 4, u)) + tr_half));
+      (__attribute__((address_space(3))) v4s*)(base + (hi0 ^ ((uint32_t)t << 5))));
   return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -393,22 +399,26 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
     // that the reads overlap the S products, the exchange and the softmax; the
     // rest (paged storage keeps more registers live) just before the products
     // that use them.
-    constexpr int kEarly = PAGED ? 8 : 14;
-    const uint4* vrows = window ? sh.vbuf : sh.kbuf;    // values: the latent rows themselves, or the window's
+    constexpr int kEarly = PAGED ? 8 : 16;
+    // values: the latent rows themselves (kbuf), or the window's (vbuf); the
+    // buffer's offset in the shared block is added before the XORs, which leave
+    // its bits alone. (The bases are made opaque per step so that the compiler
+    // does not keep 28 tile addresses live across the loop.)
+    const uint32_t vofs = window ? (uint32_t)offsetof(AttnShared<NHG>, vbuf) : (uint32_t)offsetof(AttnShared<NHG>, kbuf);
+    uint32_t vlo = vofs + vt_byte(hc, hcol, 8 * g + (hcol >> 2)), vhi = vofs + vt_byte(hc, hcol, 8 * g + (hcol >> 2) + 4);
+    asm volatile("" : "+v"(vlo), "+v"(vhi));
     v8bf vt[16];
 #pragma unroll
-    for (int t = 0; t < kEarly; ++t) vt[t] = read_vt(vrows, hc, g, hcol, t);
+    for (int t = 0; t < kEarly; ++t) vt[t] = read_vt(sh, vlo, vhi, t);
     __builtin_amdgcn_sched_barrier(0);
     {
-      float4* mine = reinterpret_cast<float4*>(&sh.sp[hg][hc][lane][0]);
-      mine[0] = make_float4(s0[0], s0[1], s0[2], s0[3]);
-      mine[1] = make_float4(s1[0], s1[1], s1[2], s1[3]);
+      sh.sp[hg][hc][0][lane] = make_float4(s0[0], s0[1], s0[2], s0[3]);
+      sh.sp[hg][hc][1][lane] = make_float4(s1[0], s1[1], s1[2], s1[3]);
     }
     __syncthreads();
     // full S: the two halves added in the same order in both waves
-    const float4* h0 = reinterpret_cast<const float4*>(&sh.sp[hg][0][lane][0]);
-    const float4* h1 = reinterpret_cast<const float4*>(&sh.sp[hg][1][lane][0]);
-    const float4 a0 = h0[0], a1 = h0[1], b0 = h1[0], b1 = h1[1];
+    const float4 a0 = sh.sp[hg][0][0][lane], a1 = sh.sp[hg][0][1][lane];
+    const float4 b0 = sh.sp[hg][1][0][lane], b1 = sh.sp[hg][1][1][lane];
     const float sa[4] = {a0.x + b0.x, a0.y + b0.y, a0.z + b0.z, a0.w + b0.w};
     const float sb[4] = {a1.x + b1.x, a1.y + b1.y, a1.z + b1.z, a1.w + b1.w};
     // lane holds rows 8g+2i (sa[i]) and 8g+2i+1 (sb[i]) for its head
@@ -447,7 +457,7 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
       plo[i] = (__bf16)(p[i] - (float)h);
     }
 #pragma unroll
-    for (int t = kEarly; t < 16; ++t) vt[t] = read_vt(vrows, hc, g, hcol, t);
+    for (int t = kEarly; t < 16; ++t) vt[t] = read_vt(sh, vlo, vhi, t);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[t], phi, o[t], 0, 0, 0);
