@@ -269,6 +269,31 @@ __device__ __forceinline__ void commit_window(AttnShared<NHG>& sh, const RawWind
   }
 }
 
+// A tail window chunk (one that follows the sparse ones) straight from HBM
+// into the chunk buffers, with no registers in between: one 16-byte
+// global_load_lds per lane and row fills a whole 1 KB row, lane L writing
+// unit slot L, so lane L loads the unit that the row's swizzle puts there.
+// With 8 waves, wave w loads rows 4w .. 4w+3 of keys and values. A row past
+// the query's window reads window row 0 instead: its products are masked and
+// its values multiply a zero P. The valid bits are written by the caller.
+template <int NHG>
+__device__ __forceinline__ void window_to_lds(const AttnArgs& a, const QueryInfo& Q, AttnShared<NHG>& sh, int c,
+                                              int wave, int lane) {
+  static_assert(NHG == 4, "8 waves x 4 rows cover a chunk");
+  const int w = __builtin_amdgcn_readfirstlane(wave);   // rows, and so their addresses, are wave-uniform
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int r = 4 * w + rr;
+    const int wr = (c - Q.cs) * kChunk + r;
+    const int64_t row = window_row(a, Q, wr < Q.n_w ? wr : 0);
+    const uint32_t ofs = 16u * (uint32_t)(lane ^ row_swizzle(r));
+    __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(a.swa_k + row * kAttnC) + ofs),
+                                     (__attribute__((address_space(3))) void*)&sh.kbuf[r * 64], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(a.swa_v + row * kAttnC) + ofs),
+                                     (__attribute__((address_space(3))) void*)&sh.vbuf[r * 64], 16, 0, 0);
+  }
+}
+
 // V^T operand of channel tile t (channels 256hc + 16t .. +15, chunk rows
 // 8g .. 8g+7) by two transposing reads: lane 4a+b of a 16-lane group gets
 // element b of the 8-byte words addressed by lanes a, 4+a, 8+a, 12+a, so lane
@@ -358,6 +383,10 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   if constexpr (PER == 1) {
     if (nW > 0) commit_window<NHG>(sh, rw);   // the loop's first barrier publishes it
   }
+  // Tail window chunks go straight into LDS, issued one step ahead (after the
+  // exchange barrier, when every wave has read the buffers; with paged storage
+  // some V reads come later, so there they are loaded at their commit).
+  constexpr bool kWinToLds = PER == 1 && !PAGED;
   for (int step = 0; step < nT; ++step) {
     const int i = step - w0;              // sparse ordinal when i < nS
     const bool window = step < w0 || i >= nS;
@@ -370,6 +399,17 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
       }
     } else if (i < nS) {
       commit_sparse<NHG, FMT>(sh, rs);
+    } else if constexpr (kWinToLds) {
+      // its rows were loaded into the buffers during the step before; set its
+      // valid bits and wait for this wave's share of the rows
+      if (threadIdx.x < kChunk / 4) {
+        const int wr0 = (split + (i + 1) * ns_ - Q.cs) * kChunk + 4 * (int)threadIdx.x;
+        uint32_t bits = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bits |= (uint32_t)(wr0 + r < Q.n_w) << r;
+        sh.vb[threadIdx.x] = bits;
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
       RawWindow tw[PER];
       load_window<NHG>(a, Q, split + (i + 1) * ns_, tw);   // window ordinal i - nS + 1
@@ -416,6 +456,11 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
       sh.sp[hg][hc][1][lane] = make_float4(s1[0], s1[1], s1[2], s1[3]);
     }
     __syncthreads();
+    if constexpr (kWinToLds) {
+      // every wave has read this step's buffers: the next step's chunk, when it
+      // is a tail window chunk (window ordinal i - nS + 2), starts loading
+      if (step + 1 < nT && i + 1 >= nS) window_to_lds<NHG>(a, Q, sh, split + (i + 2) * ns_, wave, lane);
+    }
     // full S: the two halves added in the same order in both waves
     const float4 a0 = sh.sp[hg][0][0][lane], a1 = sh.sp[hg][0][1][lane];
     const float4 b0 = sh.sp[hg][1][0][lane], b1 = sh.sp[hg][1][1][lane];
