@@ -347,17 +347,21 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   float m_use = -__builtin_inff(), l_run = 0.0f;   // P is formed as exp2(x - m_use)
 
   // This split's chunks are split + i * n_split: nS sparse ones, then nW window
-  // ones. The first window chunk is loaded with the first sparse chunk and
-  // computed first; the sparse chunks follow, each loaded while the one before
-  // it is computed; further window chunks (only with few splits) are loaded
-  // when they are committed. Only sparse loads are issued inside the loop.
+  // ones. The first window chunk is loaded in the prologue and computed first;
+  // the sparse chunks follow, each loaded a step before its commit (the first
+  // one during the window step); further window chunks (only with few splits)
+  // go straight into LDS a step ahead, or with paged storage are loaded when
+  // they are committed.
   const int ns_ = a.n_split;
   const int nS = split < Q.cs ? (Q.cs - split + ns_ - 1) / ns_ : 0;
   const int nT = split < nchunk ? (nchunk - split + ns_ - 1) / ns_ : 0;
   const int nW = nT - nS, w0 = nW > 0 ? 1 : 0;
-  RawSparse rs[PER];
+  // With a window chunk first, the first sparse chunk is loaded in the loop's
+  // first step (like every later one, a step ahead of its commit), so that the
+  // prologue waits for one round of loads only.
+  RawSparse rs[PER] = {};
   RawWindow rw[PER];
-  if (nS > 0) load_sparse<NHG, FMT, PAGED>(a, Q, qi, split, 0, lp, rs);
+  if (nS > 0 && w0 == 0) load_sparse<NHG, FMT, PAGED>(a, Q, qi, split, 0, lp, rs);
   // (with several items per thread the window slot would not fit in registers
   // beside the accumulators: the first window chunk is then loaded at commit)
   if constexpr (PER == 1) {
@@ -416,7 +420,7 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
       commit_window<NHG>(sh, tw);
     }
     __syncthreads();
-    if (step >= w0 && i + 1 < nS) load_sparse<NHG, FMT, PAGED>(a, Q, qi, split + (i + 1) * ns_, i + 1, lp, rs);
+    if (i + 1 < nS) load_sparse<NHG, FMT, PAGED>(a, Q, qi, split + (i + 1) * ns_, i + 1, lp, rs);
 
     // partial S^T over this channel half: A = even rows (tile 0) / odd rows (tile 1), B = Q^T
     // (all 16 K reads are issued before the first product, so that the
