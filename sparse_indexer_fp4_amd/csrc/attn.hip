@@ -55,7 +55,7 @@ struct AttnShared {
   uint4 kbuf[kRowUnits];                 // row-major bf16 keys (= values for sparse rows): 32 KB
   uint4 vbuf[kRowUnits];                 // row-major bf16 values of a window chunk: 32 KB
   float4 sp[NHG][2][2][64];              // partial S of each head group's two channel halves, [tile][lane]
-  uint32_t vb[kChunk / 4];               // bit r of word q: chunk row 4q+r is a real row
+  uint32_t vb[2][kChunk / 4];            // bit r of word q: chunk row 4q+r is a real row (by step parity)
 };
 
 // 16-byte unit holding channels 8u..8u+7 of chunk row `row`: the unit index is
@@ -230,14 +230,14 @@ __device__ __forceinline__ float max_over_rows(float x) {
 }
 
 template <int NHG, int FMT>
-__device__ __forceinline__ void commit_sparse(AttnShared<NHG>& sh, const RawSparse (&raw)[kItems / (128 * NHG)]) {
+__device__ __forceinline__ void commit_sparse(AttnShared<NHG>& sh, int vbi, const RawSparse (&raw)[kItems / (128 * NHG)]) {
   constexpr int PER = kItems / (128 * NHG);
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
     const int item = threadIdx.x + it * 128 * NHG;
     const int rg = item_rows(item), cg = item & 63;
     const uint32_t valid = raw[it].valid;
-    if (cg == 0) sh.vb[rg] = valid;
+    if (cg == 0) sh.vb[vbi][rg] = valid;
     uint32_t d[4][4];
     dequant_item<FMT>(raw[it].code, raw[it].scale, valid, cg, d);
     store_rows(sh.kbuf, rg, cg, d);
@@ -245,14 +245,14 @@ __device__ __forceinline__ void commit_sparse(AttnShared<NHG>& sh, const RawSpar
 }
 
 template <int NHG>
-__device__ __forceinline__ void commit_window(AttnShared<NHG>& sh, const RawWindow (&raw)[kItems / (128 * NHG)]) {
+__device__ __forceinline__ void commit_window(AttnShared<NHG>& sh, int vbi, const RawWindow (&raw)[kItems / (128 * NHG)]) {
   constexpr int PER = kItems / (128 * NHG);
 #pragma unroll
   for (int it = 0; it < PER; ++it) {
     const int item = threadIdx.x + it * 128 * NHG;
     const int rg = item_rows(item), cg = item & 63;
     const uint32_t valid = raw[it].valid;
-    if (cg == 0) sh.vb[rg] = valid;
+    if (cg == 0) sh.vb[vbi][rg] = valid;
     uint32_t d[4][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -350,15 +350,16 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
   // ones. The first window chunk is loaded in the prologue and computed first;
   // the sparse chunks follow, each loaded a step before its commit (the first
   // one during the window step); further window chunks (only with few splits)
-  // go straight into LDS a step ahead, or with paged storage are loaded when
-  // they are committed.
+  // go straight into LDS a step ahead (with several items per thread, they are
+  // loaded when they are committed).
   const int ns_ = a.n_split;
   const int nS = split < Q.cs ? (Q.cs - split + ns_ - 1) / ns_ : 0;
   const int nT = split < nchunk ? (nchunk - split + ns_ - 1) / ns_ : 0;
   const int nW = nT - nS, w0 = nW > 0 ? 1 : 0;
-  // With a window chunk first, the first sparse chunk is loaded in the loop's
-  // first step (like every later one, a step ahead of its commit), so that the
-  // prologue waits for one round of loads only.
+  // With a window chunk first, the first sparse chunk is loaded after that
+  // chunk's commit (it is committed at the end of the window step, like every
+  // later one a step after its load), so that the prologue waits for one round
+  // of loads only.
   RawSparse rs[PER] = {};
   RawWindow rw[PER];
   if (nS > 0 && w0 == 0) load_sparse<NHG, FMT, PAGED>(a, Q, qi, split, 0, lp, rs);
@@ -384,43 +385,32 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
         asm volatile("" ::"v"(__builtin_bit_cast(u32x4, rw[it].k[r])), "v"(__builtin_bit_cast(u32x4, rw[it].v[r])));
     }
   }
-  if constexpr (PER == 1) {
-    if (nW > 0) commit_window<NHG>(sh, rw);   // the loop's first barrier publishes it
+  // Step 0's chunk is committed here. Every step then ends by committing the
+  // next step's chunk: all of its own LDS reads of the chunk buffers are done
+  // before its exchange barrier, so the buffers are free from there on, and a
+  // step needs two barriers, one that publishes its chunk and one for the S
+  // exchange. (The valid bits alternate between two slots, since a wave that
+  // commits may run ahead of one still forming this step's P.)
+  if (w0) {
+    if constexpr (PER == 1) {
+      commit_window<NHG>(sh, 0, rw);
+    } else {
+      RawWindow tw[PER];
+      load_window<NHG>(a, Q, split + nS * ns_, tw);
+      commit_window<NHG>(sh, 0, tw);
+    }
+    if (nS > 0) load_sparse<NHG, FMT, PAGED>(a, Q, qi, split, 0, lp, rs);
+  } else if (nS > 0) {
+    commit_sparse<NHG, FMT>(sh, 0, rs);
+    if (nS > 1) load_sparse<NHG, FMT, PAGED>(a, Q, qi, split + ns_, 1, lp, rs);
   }
-  // Tail window chunks go straight into LDS, issued one step ahead (after the
-  // exchange barrier, when every wave has read the buffers; with paged storage
-  // some V reads come later, so there they are loaded at their commit).
-  constexpr bool kWinToLds = PER == 1 && !PAGED;
+  // Tail window chunks go straight into LDS, issued one step ahead.
+  constexpr bool kWinToLds = PER == 1;
   for (int step = 0; step < nT; ++step) {
     const int i = step - w0;              // sparse ordinal when i < nS
     const bool window = step < w0 || i >= nS;
+    const int vbi = step & 1;
     __syncthreads();
-    if (step < w0) {
-      if constexpr (PER != 1) {          // (with one item per thread it was committed before the loop)
-        RawWindow tw[PER];
-        load_window<NHG>(a, Q, split + nS * ns_, tw);
-        commit_window<NHG>(sh, tw);
-      }
-    } else if (i < nS) {
-      commit_sparse<NHG, FMT>(sh, rs);
-    } else if constexpr (kWinToLds) {
-      // its rows were loaded into the buffers during the step before; set its
-      // valid bits and wait for this wave's share of the rows
-      if (threadIdx.x < kChunk / 4) {
-        const int wr0 = (split + (i + 1) * ns_ - Q.cs) * kChunk + 4 * (int)threadIdx.x;
-        uint32_t bits = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bits |= (uint32_t)(wr0 + r < Q.n_w) << r;
-        sh.vb[threadIdx.x] = bits;
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else {
-      RawWindow tw[PER];
-      load_window<NHG>(a, Q, split + (i + 1) * ns_, tw);   // window ordinal i - nS + 1
-      commit_window<NHG>(sh, tw);
-    }
-    __syncthreads();
-    if (i + 1 < nS) load_sparse<NHG, FMT, PAGED>(a, Q, qi, split + (i + 1) * ns_, i + 1, lp, rs);
 
     // partial S^T over this channel half: A = even rows (tile 0) / odd rows (tile 1), B = Q^T
     // (all 16 K reads are issued before the first product, so that the
@@ -439,21 +429,19 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kr0[kk]), b, s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kr1[kk]), b, s1, 0, 0, 0);
     }
-    // V^T operands of the 16 channel tiles. The first kEarly are read now, so
-    // that the reads overlap the S products, the exchange and the softmax; the
-    // rest (paged storage keeps more registers live) just before the products
-    // that use them.
-    constexpr int kEarly = PAGED ? 8 : 16;
-    // values: the latent rows themselves (kbuf), or the window's (vbuf); the
+    // V^T operands of all 16 channel tiles, read now (before the exchange
+    // barrier, which then also ends this step's use of the chunk buffers), so
+    // that the reads overlap the S products, the exchange and the softmax.
+    // Values: the latent rows themselves (kbuf), or the window's (vbuf); the
     // buffer's offset in the shared block is added before the XORs, which leave
     // its bits alone. (The bases are made opaque per step so that the compiler
-    // does not keep 28 tile addresses live across the loop.)
+    // does not keep 32 tile addresses live across the loop.)
     const uint32_t vofs = window ? (uint32_t)offsetof(AttnShared<NHG>, vbuf) : (uint32_t)offsetof(AttnShared<NHG>, kbuf);
     uint32_t vlo = vofs + vt_byte(hc, hcol, 8 * g + (hcol >> 2)), vhi = vofs + vt_byte(hc, hcol, 8 * g + (hcol >> 2) + 4);
     asm volatile("" : "+v"(vlo), "+v"(vhi));
     v8bf vt[16];
 #pragma unroll
-    for (int t = 0; t < kEarly; ++t) vt[t] = read_vt(sh, vlo, vhi, t);
+    for (int t = 0; t < 16; ++t) vt[t] = read_vt(sh, vlo, vhi, t);
     __builtin_amdgcn_sched_barrier(0);
     {
       sh.sp[hg][hc][0][lane] = make_float4(s0[0], s0[1], s0[2], s0[3]);
@@ -473,7 +461,7 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
     // lane holds rows 8g+2i (sa[i]) and 8g+2i+1 (sb[i]) for its head
     uint32_t valid = 0;
 #pragma unroll
-    for (int q = 0; q < kChunk / 4; ++q) valid |= sh.vb[q] << (4 * q);
+    for (int q = 0; q < kChunk / 4; ++q) valid |= sh.vb[vbi][q] << (4 * q);
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -484,8 +472,8 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 1; i < 8; ++i) cm = fmaxf(cm, x[i]);
     cm = max_over_rows(cm);
-    if (cm == -__builtin_inff() && m_use == -__builtin_inff()) continue;   // nothing usable yet (per head)
-    // move the reference maximum only when this chunk exceeds it by more than 2^8
+    // move the reference maximum only when this chunk exceeds it by more than
+    // 2^8 (always at a head's first usable row: m_use starts at -inf)
     const bool move = cm > m_use + 8.0f;
     if (__builtin_amdgcn_ballot_w64(move)) {
       const float corr = move ? __builtin_amdgcn_exp2f(m_use - cm) : 1.0f;
@@ -494,9 +482,13 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int t = 0; t < 16; ++t) o[t] *= corr;
     }
+    // m_use stays -inf while a head has seen no usable row; its x are all -inf
+    // then, and so are its P zeros (its rows are zeros too: rows that are not
+    // real are committed as zeros, or multiply a zero P)
+    const float m_sub = m_use == -__builtin_inff() ? 0.0f : m_use;
     float p[8], psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - m_use); psum += p[i]; }
+    for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - m_sub); psum += p[i]; }
     l_run += psum;
     v8bf phi, plo;
 #pragma unroll
@@ -506,11 +498,34 @@ __global__ __launch_bounds__(128 * NHG) void attn_kernel(AttnArgs a) {
       plo[i] = (__bf16)(p[i] - (float)h);
     }
 #pragma unroll
-    for (int t = kEarly; t < 16; ++t) vt[t] = read_vt(sh, vlo, vhi, t);
-#pragma unroll
     for (int t = 0; t < 16; ++t) {
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[t], phi, o[t], 0, 0, 0);
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[t], plo, o[t], 0, 0, 0);
+    }
+
+    // the next step's chunk: a sparse chunk from the registers loaded a step
+    // ago (whose slot then takes the loads of the sparse chunk after it); a
+    // tail window chunk, already on its way into the buffers, gets its valid
+    // bits and this wave waits for its share of the rows
+    if (step + 1 < nT) {
+      const int i1 = i + 1;
+      if (i1 < nS) {
+        commit_sparse<NHG, FMT>(sh, vbi ^ 1, rs);
+        if (i1 + 1 < nS) load_sparse<NHG, FMT, PAGED>(a, Q, qi, split + (i1 + 1) * ns_, i1 + 1, lp, rs);
+      } else if constexpr (kWinToLds) {
+        if (threadIdx.x < kChunk / 4) {
+          const int wr0 = (split + (i1 + 1) * ns_ - Q.cs) * kChunk + 4 * (int)threadIdx.x;
+          uint32_t bits = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bits |= (uint32_t)(wr0 + r < Q.n_w) << r;
+          sh.vb[vbi ^ 1][threadIdx.x] = bits;
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else {
+        RawWindow tw[PER];
+        load_window<NHG>(a, Q, split + (i1 + 1) * ns_, tw);   // window ordinal i1 - nS + 1
+        commit_window<NHG>(sh, vbi ^ 1, tw);
+      }
     }
   }
 
