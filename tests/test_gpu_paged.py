@@ -116,14 +116,18 @@ def test_paged_appends_and_ring(fk, gpu, fmt):
         assert np.array_equal(bf16_to_f64(ring_v[s].cpu()), paged.ring_after_appends(bf16_to_f64(wv_rows[s]), W))
 
 
+@pytest.mark.parametrize("k,W", [(512, 128), (64, 600)], ids=["k512-W128", "k64-W600"])
 @pytest.mark.parametrize("page_rows", [64, 256])
 @pytest.mark.parametrize("fmt", [kvformats.FMT_FP4, kvformats.FMT_MXFP4, kvformats.FMT_FP8], ids=["fp4", "mxfp4", "fp8"])
-def test_paged_decode_path(fk, gpu, page_rows, fmt):
+def test_paged_decode_path(fk, gpu, page_rows, fmt, k, W):
     """Full and Reindex indexer and decode attention through pages equal the
-    contiguous path bit for bit, and the oracle."""
-    _say(f"paged decode path page_rows={page_rows} fmt={fmt}")
+    contiguous path bit for bit, and the oracle. With k = 64 and a 600-row
+    window the launch takes 16 splits, and those that hold two window chunks
+    load the second one a step ahead, from the ring (and its last chunk is
+    partial)."""
+    _say(f"paged decode path page_rows={page_rows} fmt={fmt} k={k} W={W}")
     lengths = [5000, 1500, 64, 9001]
-    H, D, C, Hq, P, k, W = 16, 128, 512, 64, 256, 512, 128
+    H, D, C, Hq, P = 16, 128, 512, 64, 256
     seed = 30 + page_rows + fmt
     n_seq = len(lengths)
     bt, n_pages = _block_tables(lengths, page_rows, spare=2, seed=seed)
