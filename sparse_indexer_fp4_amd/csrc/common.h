@@ -39,10 +39,12 @@ __host__ __device__ constexpr float e4m3_value(uint32_t c) {
 // (DPP: swap neighbours, swap pairs, then mirror the halves of each 8 lanes;
 // med3(x, y, FLT_MAX) is max(x, y) without quieting).
 __device__ __forceinline__ float max8(float v) {
+  // (every lane reads a lane of its own row in these patterns, so the moves
+  // need no old value, and none is copied into their destinations first)
   int x = __float_as_int(v);
-  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false)), 3.402823466e38f));
-  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false)), 3.402823466e38f));
-  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false)), 3.402823466e38f));
+  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true)), 3.402823466e38f));
+  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true)), 3.402823466e38f));
+  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true)), 3.402823466e38f));
   return __int_as_float(x);
 }
 
