@@ -36,16 +36,17 @@ __host__ __device__ constexpr float e4m3_value(uint32_t c) {
 }
 
 // Maximum over each aligned group of 8 lanes, left in every lane of the group
-// (DPP: swap neighbours, swap pairs, then mirror the halves of each 8 lanes;
-// med3(x, y, FLT_MAX) is max(x, y) without quieting).
+// (swap neighbours, swap pairs, then mirror the halves of each 8 lanes). Each
+// step is one v_max_f32 whose first operand is read through DPP; the s_nop
+// gives the two wait states a DPP read needs after a VALU write. The inputs
+// are finite here (scores, or -FLT_MAX for a token that is not visible), so
+// max has no NaN case to handle.
 __device__ __forceinline__ float max8(float v) {
-  // (every lane reads a lane of its own row in these patterns, so the moves
-  // need no old value, and none is copied into their destinations first)
-  int x = __float_as_int(v);
-  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true)), 3.402823466e38f));
-  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true)), 3.402823466e38f));
-  x = __float_as_int(__builtin_amdgcn_fmed3f(__int_as_float(x), __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true)), 3.402823466e38f));
-  return __int_as_float(x);
+  float r;
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "=v"(v) : "v"(r));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(v));
+  return r;
 }
 
 }  // namespace fp4kv
