@@ -85,6 +85,13 @@ struct RegKeys {
   }
 };
 
+// Keys of two pool slots held by the calling thread (2,048 slots at most).
+struct PairKeys {
+  static constexpr int kRun = 2;
+  uint32_t k[2];
+  template <typename F> __device__ __forceinline__ void each(F f) const { f(0, k[0]); f(1, k[1]); }
+};
+
 // Keys of the calling thread's run of 16 consecutive block maxima (coalesced
 // across the wave), key 0 past the end n.
 __device__ __forceinline__ void load_run(const float* bm, int64_t n, int64_t i0, uint32_t (&k)[kKPT]) {
@@ -338,19 +345,27 @@ __global__ __launch_bounds__(kSelThreads, WIDE ? 4 : 8) void select_kernel(Selec
   // unchanged, ties included).
   uint32_t tmin = 0u;
   if (!REINDEX) {
-    // ---- blocks -> pool. Two workgroups per query run side by side: role 0
-    // (blockIdx.y == 0) selects and writes the pool; role 1 selects the k
-    // positions. When the pool holds >= k blocks, role 1 needs only the k best
-    // blocks, not the whole pool: every position of the global top-k over all
-    // visible positions lies in one of them (each block ranked ahead of its
-    // block holds a distinct position ranked ahead of it: its best one, ahead
-    // on score or, on a tie, on the lower position), and that global top-k is
-    // then the pool's top-k. So role 1 ranks the blocks for a pool of
-    // min(k, blocks) and searches 8k positions instead of 8P.
-    const bool idx_role = blockIdx.y == 1;
+    // ---- blocks -> pool. When the pool holds >= k blocks, the position search
+    // needs only the k best blocks, not the whole pool: every position of the
+    // global top-k over all visible positions lies in one of them (each block
+    // ranked ahead of its block holds a distinct position ranked ahead of it:
+    // its best one, ahead on score or, on a tie, on the lower position), and
+    // that global top-k is then the pool's top-k.
+    // With two workgroups per query (grid y = 2: few queries) they run side by
+    // side: role 0 (blockIdx.y == 0) selects and writes the pool; role 1 ranks
+    // the blocks for a pool of min(k, blocks) and searches those 8k positions.
+    // With one (grid y = 1: more queries than the chip runs two workgroups of
+    // at once) a workgroup writes the pool and then narrows it to its k best
+    // blocks: the pool is the first P blocks in the order (maximum descending,
+    // index ascending) and the k best blocks are the first k, so ranking the
+    // pool's blocks gives role 1's blocks, ties included, without a second
+    // search over every block maximum.
+    const bool split_roles = gridDim.y == 2;
+    const bool idx_role = !split_roles || blockIdx.y == 1;
+    const bool pool_role = !split_roles || blockIdx.y == 0;
     const int64_t nblk = (n_vis + 7) / 8;
     const float* bm = a.blockmax + (int64_t)qi * a.nblk_max;
-    const int kk = (int)min<int64_t>(idx_role && a.P >= a.k ? a.k : a.P, nblk);
+    const int kk = (int)min<int64_t>(split_roles && idx_role && a.P >= a.k ? a.k : a.P, nblk);
     npool = 0;
     if (kk > 0 && nblk <= kRegKeys) {
       RegKeys keys;
@@ -369,13 +384,33 @@ __global__ __launch_bounds__(kSelThreads, WIDE ? 4 : 8) void select_kernel(Selec
       npool = compact_chunks(sh, keys, T, take_eq, [&](int slot, int64_t b) { sh.pool[slot] = (int32_t)b; });
       tmin = T;
     }
-    if (npool < a.k) tmin = 0u;
     __syncthreads();
-    if (!idx_role) {
+    if (pool_role) {
       for (int i = tid; i < a.P; i += kSelThreads) pool_row[i] = i < npool ? sh.pool[i] : -1;
       if (tid == 0) a.n_pool[qi] = npool;
-      return;
+      if (!idx_role) return;
     }
+    if (!split_roles && a.P >= a.k && npool > a.k) {
+      // narrow the pool (at most 2,048 slots: two per thread) to its k best
+      // blocks, in place and in pool order; the keys come back from the block
+      // maxima. Every slot is read here, before the barrier in
+      // candidate_summary, and written only by the compaction after it.
+      PairKeys pk;
+      int32_t pb[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int jb = 2 * tid + h;
+        pb[h] = jb < npool ? sh.pool[jb] : 0;
+        pk.k[h] = jb < npool ? float_key(bm[pb[h]]) : 0u;
+      }
+      uint32_t vor, vand, T; int cnt, take_eq;
+      candidate_summary(sh, pk, vor, vand, cnt);
+      radix_threshold(sh, pk, a.k, vor, vand, T, take_eq);
+      npool = compact_selected(sh, pk, T, take_eq, [&](int slot, int j) { sh.pool[slot] = pb[j]; });
+      tmin = T;
+      __syncthreads();
+    }
+    if (npool < a.k) tmin = 0u;
   } else {
     npool = a.n_pool[qi];
     npool = npool < 0 ? 0 : (npool > a.P ? a.P : npool);
@@ -434,8 +469,11 @@ __global__ __launch_bounds__(kSelThreads, WIDE ? 4 : 8) void select_kernel(Selec
 hipError_t launch_select(const SelectArgs& a, int n_q, bool reindex, hipStream_t stream) {
   if (n_q == 0) return hipSuccess;
   // Full: two workgroups per query (pool, positions), the query index fastest
-  // so that both land on the same XCD. Reindex: one (the pool is given).
-  const int roles = reindex ? 1 : 2;
+  // so that both land on the same XCD, while every workgroup fits on the chip
+  // at once (two per CU); beyond that one per query does both in turn, which
+  // searches the block maxima once instead of twice. Reindex: one (the pool is
+  // given).
+  const int roles = reindex || n_q > kSelWideQueries ? 1 : 2;
   const bool wide = (int64_t)n_q * roles <= kSelWideQueries;
   const dim3 grid((uint32_t)n_q, (uint32_t)roles);
   if (reindex && wide)

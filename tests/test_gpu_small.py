@@ -408,6 +408,20 @@ def test_index_full_many_queries_narrow_selection(fk, gpu, P, k):
     _indexer_case(fk, gpu, lengths, 4, 64, P, k, seed=31, lo=-1, hi=1)
 
 
+@pytest.mark.parametrize("lo,hi", [(-8, 8), (-1, 1)])
+def test_index_full_one_workgroup_per_query_long(fk, gpu, lo, hi):
+    """260 queries of one 140,000-token sequence (one selection workgroup per
+    query, which writes the pool and then narrows it to its k best blocks),
+    positions on both sides of 16,384 blocks (block maxima in registers or
+    re-read in chunks), P >= k, and heavy ties in the second case: every
+    query's pool and indices against the oracle."""
+    _say(f"index_full 260 queries, one workgroup each, long contexts, values {lo}..{hi}")
+    rng = np.random.default_rng(67)
+    L = 140000
+    positions = sorted(int(x) for x in rng.integers(100000, L, 260))
+    _indexer_case(fk, gpu, [L], 4, 64, 2048, 512, seed=67, lo=lo, hi=hi, q_per_seq=260, positions=positions)
+
+
 def test_repeatable_bits_attention_and_append(fk, gpu):
     """Attention (split partials + combine) and the quantize-append give
     identical bits when run twice on the same inputs."""
