@@ -214,7 +214,7 @@ static fp4kv_status launch_scores(const void* idx_q, const float* w, const void*
   sa.nblk_max = nblk_of(max_ctx, block);
   // Many queries per sequence share every key: the scan is a dense product on the matrix cores
   // (contiguous storage only; a paged cache is scanned query by query).
-  if (!map && fp4kv::scan_mfma_supported(H, D, q_per_seq) && max_ctx <= INT32_MAX) {
+  if (!map && fp4kv::scan_mfma_supported(H, D, q_per_seq, max_ctx)) {
     if (app && app->n_rows > 0) {          // the matrix-core scan does not carry an append: it goes first
       hipError_t e = fp4kv::launch_quantize_append(app->fmt, app->src, app->n_rows, app->C, app->dd, app->codes,
                                                    app->scales, app->cap_rows, s);

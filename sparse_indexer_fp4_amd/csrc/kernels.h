@@ -165,7 +165,7 @@ bool scan_supported(int H, int D);
 hipError_t launch_scan(ScanArgs a, int H, int D, int n_q, int64_t slots, bool reindex, hipStream_t stream,
                        const AppendJob* app = nullptr);
 // Matrix-core Full scan for sequences with many queries (q_per_seq >= 16).
-bool scan_mfma_supported(int H, int D, int q_per_seq);
+bool scan_mfma_supported(int H, int D, int q_per_seq, int64_t max_ctx);
 hipError_t launch_scan_mfma(ScanArgs a, int H, int D, int n_q, hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, int n_q, bool reindex, hipStream_t stream);
 size_t attn_workspace_bytes(int nq, int Hq, int k, int W);

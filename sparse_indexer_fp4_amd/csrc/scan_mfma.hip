@@ -154,21 +154,30 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a, MfmaSc
       wv[j][i] = (valid && h < g.H) ? a.w[(int64_t)q * g.H + h] : 0.0f;
     }
   }
-  // visible-token limits of the queries whose scores this lane will hold (query 2jp + lane/32)
-  const int32_t lim[2] = {nvis[4 * wave + (lane >> 5)], nvis[4 * wave + 2 + (lane >> 5)]};
-  float* srow[2];                             // score and block-maximum rows of query 2jp + lane/32
-  float* bmrow[2];
+  // This lane's token of each 32-token part is t0 + 32 part + lane % 32, its
+  // scores belong to query 2jp + lane/32. The wave's four score and
+  // block-maximum rows start at uniform bases; carried from tile to tile are
+  // 32-bit byte offsets from them to that token's score and block maximum in
+  // part 0 (parts add immediate offsets; four rows of max_ctx < 2^28 tokens
+  // keep them below 2^32) and how many of the query's visible tokens lie at or
+  // past it.
+  const int qw = q0 + 4 * __builtin_amdgcn_readfirstlane(wave);
+  char* const sbase = reinterpret_cast<char*>(a.scores + (int64_t)qw * a.max_ctx);
+  char* const bbase = reinterpret_cast<char*>(a.blockmax + (int64_t)qw * a.nblk_max);
+  uint32_t so[2], bo[2];
+  int32_t rem[2];
 #pragma unroll
   for (int jp = 0; jp < 2; ++jp) {
-    const int64_t q = q0 + 4 * wave + 2 * jp + (lane >> 5);
-    srow[jp] = a.scores + q * a.max_ctx;
-    bmrow[jp] = a.blockmax + q * a.nblk_max;
+    const int64_t row = 2 * jp + (lane >> 5);
+    const int64_t tb = r0 + (lane & 31);      // r0 is a multiple of 128: tb / 8 is the lane's block
+    so[jp] = (uint32_t)((row * a.max_ctx + tb) * 4);
+    bo[jp] = (uint32_t)((row * a.nblk_max + (tb >> 3)) * 4);
+    rem[jp] = (int32_t)(nvis[4 * wave + row] - tb);
   }
   tile_barrier();
 
   for (int st = 0; st < nsteps; ++st) {
     const uint4* tile = ring[st % kMRing];
-    const int64_t t0 = r0 + (int64_t)st * kMTile;
 #pragma unroll
     for (int part = 0; part < kMTile / 32; ++part) {
       uint4 bf[2][KS];                        // B operand: K[token col of tile tt][32ks + 8g4 .. +7]
@@ -222,19 +231,24 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a, MfmaSc
         // rows of 16 lanes: (A, tile 0), (A, tile 1), (B, tile 0), (B, tile 1); all four head groups summed
         const auto yy = __builtin_amdgcn_permlane16_swap(__float_as_uint(sa), __float_as_uint(sb), false, false);
         const float y = __uint_as_float(yy[0]) + __uint_as_float(yy[1]);
-        const int64_t t = t0 + 32 * part + (lane & 31);
-        const bool vis = t < lim[jp];
-        if (vis) srow[jp][t] = y;
+        const bool vis = 32 * part < rem[jp];
+        if (vis) reinterpret_cast<float*>(sbase + so[jp])[32 * part] = y;
         const float bm = max8(vis ? y : -3.402823466e38f);
-        if ((lane & 7) == 0 && vis) bmrow[jp][t >> 3] = bm;
+        if ((lane & 7) == 0 && vis) reinterpret_cast<float*>(bbase + bo[jp])[4 * part] = bm;
       }
+    }
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      so[jp] += kMTile * 4;
+      bo[jp] += kMTile / 8 * 4;
+      rem[jp] -= kMTile;
     }
     tile_barrier();
   }
 }
 
-bool scan_mfma_supported(int H, int D, int q_per_seq) {
-  return q_per_seq >= 16 && H <= 16 && (D == 64 || D == 128);
+bool scan_mfma_supported(int H, int D, int q_per_seq, int64_t max_ctx) {
+  return q_per_seq >= 16 && H <= 16 && (D == 64 || D == 128) && max_ctx < (int64_t(1) << 28) - 1024;
 }
 
 hipError_t launch_scan_mfma(ScanArgs a, int H, int D, int n_q, hipStream_t stream) {
