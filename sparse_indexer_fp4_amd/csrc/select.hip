@@ -317,6 +317,73 @@ __device__ int compact_chunks(SelShared& sh, const GlobalKeys& keys, uint32_t T,
   return filled;
 }
 
+// Keys of KPT consecutive token candidates per thread.
+template <int KPT>
+struct TokenKeys {
+  static constexpr int kRun = KPT;
+  uint32_t k[KPT];
+  template <typename F> __device__ __forceinline__ void each(F f) const {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) f(j, k[j]);
+  }
+};
+
+// Top-k positions among the positions of the npool blocks in sh.pool
+// (ascending), dropping those whose key is below tmin. Candidate c (< npool*8)
+// is position pool[c/8]*8 + c%8; thread t holds candidates KPT t .. KPT t +
+// KPT - 1, so candidates, and with them ties, run in ascending position order
+// over the threads.
+template <bool REINDEX, int KPT>
+__device__ void token_search(SelShared& sh, const SelectArgs& a, int qi, int npool, uint32_t tmin, int64_t n_vis) {
+  static_assert(KPT % 4 == 0 && KPT <= kKPT, "candidate runs of whole 4-position groups");
+  const int tid = threadIdx.x;
+  TokenKeys<KPT> keys;
+#pragma unroll
+  for (int g = 0; g < KPT / 4; ++g) {
+    const int c = tid * KPT + 4 * g;                   // first candidate of this group of 4
+    const int jb = c >> 3, e0 = c & 7;                 // pool slot, position in its block (0 or 4)
+    const int64_t b = jb < npool ? (int64_t)sh.pool[jb] : -1;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    if (REINDEX) {
+      if (jb < npool) {
+        const float4 f = *reinterpret_cast<const float4*>(a.scores + ((int64_t)qi * a.P + jb) * 8 + e0);
+        s[0] = f.x; s[1] = f.y; s[2] = f.z; s[3] = f.w;
+      }
+    } else if (b >= 0 && b * 8 + e0 + 4 <= n_vis && ((a.max_ctx & 3) == 0)) {
+      const float4 f = *reinterpret_cast<const float4*>(a.scores + (int64_t)qi * a.max_ctx + b * 8 + e0);
+      s[0] = f.x; s[1] = f.y; s[2] = f.z; s[3] = f.w;
+    } else if (b >= 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s[e] = b * 8 + e0 + e < n_vis ? a.scores[(int64_t)qi * a.max_ctx + b * 8 + e0 + e] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = b >= 0 && b * 8 + e0 + e < n_vis;
+      const uint32_t key = ok ? float_key(s[e]) : 0u;
+      keys.k[4 * g + e] = key >= tmin ? key : 0u;
+    }
+  }
+  // float_key never gives 0 for a finite score, so the candidates are the visible
+  // positions (those scoring >= tmin)
+  uint32_t vor, vand; int nvalid;
+  candidate_summary(sh, keys, vor, vand, nvalid);
+  const int kk = min(a.k, nvalid);
+  int32_t* out = a.idx_out + (int64_t)qi * a.k;
+  int nsel = 0;
+  if (kk > 0) {
+    uint32_t T; int take_eq;
+    radix_threshold(sh, keys, kk, vor, vand, T, take_eq);
+    nsel = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) {
+      const int c = tid * KPT + j;
+      sh.out[slot] = sh.pool[c >> 3] * 8 + (c & 7);
+    });
+  }
+  __syncthreads();
+  for (int i = tid; i < a.k; i += kSelThreads) out[i] = i < nsel ? sh.out[i] : -1;
+  if (tid == 0) a.n_idx[qi] = nsel;
+}
+
 // WIDE: at most one workgroup per CU is wanted (few queries), so the kernel
 // may use up to 128 VGPRs; otherwise it is held to 64, so that two 1,024-thread
 // workgroups share a CU (measured: 32 queries 18.9 against 19.7 us, 4,096
@@ -418,52 +485,11 @@ __global__ __launch_bounds__(kSelThreads, WIDE ? 4 : 8) void select_kernel(Selec
     __syncthreads();
   }
 
-  // ---- pool positions -> top-k. Candidate j (< npool*8) is position
-  // pool[j/8]*8 + j%8; thread t owns candidates 16t .. 16t+15 (two blocks).
-  RegKeys keys;
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int jb = 2 * tid + half;                     // pool slot
-    const int64_t b = jb < npool ? (int64_t)sh.pool[jb] : -1;
-    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (REINDEX) {
-      if (jb < npool) {
-        const float4* v = reinterpret_cast<const float4*>(a.scores + ((int64_t)qi * a.P + jb) * 8);
-        const float4 f0 = v[0], f1 = v[1];
-        s[0] = f0.x; s[1] = f0.y; s[2] = f0.z; s[3] = f0.w; s[4] = f1.x; s[5] = f1.y; s[6] = f1.z; s[7] = f1.w;
-      }
-    } else if (b >= 0 && b * 8 + 8 <= n_vis && ((a.max_ctx & 3) == 0)) {
-      const float4* v = reinterpret_cast<const float4*>(a.scores + (int64_t)qi * a.max_ctx + b * 8);
-      const float4 f0 = v[0], f1 = v[1];
-      s[0] = f0.x; s[1] = f0.y; s[2] = f0.z; s[3] = f0.w; s[4] = f1.x; s[5] = f1.y; s[6] = f1.z; s[7] = f1.w;
-    } else if (b >= 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] = b * 8 + e < n_vis ? a.scores[(int64_t)qi * a.max_ctx + b * 8 + e] : 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool ok = b >= 0 && b * 8 + e < n_vis;
-      const uint32_t key = ok ? float_key(s[e]) : 0u;
-      keys.k[8 * half + e] = key >= tmin ? key : 0u;
-    }
-  }
-  // float_key never gives 0 for a finite score, so the candidates are the visible
-  // positions (those scoring >= tmin)
-  uint32_t vor, vand; int nvalid;
-  candidate_summary(sh, keys, vor, vand, nvalid);
-  const int kk = min(a.k, nvalid);
-  int32_t* out = a.idx_out + (int64_t)qi * a.k;
-  int nsel = 0;
-  if (kk > 0) {
-    uint32_t T; int take_eq;
-    radix_threshold(sh, keys, kk, vor, vand, T, take_eq);
-    nsel = compact_selected(sh, keys, T, take_eq, [&](int slot, int j) {
-      sh.out[slot] = sh.pool[2 * tid + (j >> 3)] * 8 + (j & 7);
-    });
-  }
-  __syncthreads();
-  for (int i = tid; i < a.k; i += kSelThreads) out[i] = i < nsel ? sh.out[i] : -1;
-  if (tid == 0) a.n_idx[qi] = nsel;
+  // ---- pool positions -> top-k: 4 candidates per thread when they fit (a
+  // pool narrowed to k <= 512 blocks), else 16, so that no thread runs its
+  // passes over a run of empty keys
+  if (npool <= kSelThreads / 2) token_search<REINDEX, 4>(sh, a, qi, npool, tmin, n_vis);
+  else token_search<REINDEX, 16>(sh, a, qi, npool, tmin, n_vis);
 }
 
 hipError_t launch_select(const SelectArgs& a, int n_q, bool reindex, hipStream_t stream) {
