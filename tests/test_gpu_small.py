@@ -399,13 +399,25 @@ def test_repeatable_bits(fk, gpu):
 
 @pytest.mark.parametrize("P,k", [(64, 96), (64, 40)])
 def test_index_full_many_queries_narrow_selection(fk, gpu, P, k):
-    """300 queries (600 selection workgroups, the instance held to 64 VGPRs so
+    """300 queries (one selection workgroup per query, which writes the pool
+    and narrows it to the k best blocks, in the instance held to 64 VGPRs so
     that two share a CU), short ragged contexts with heavy ties, the pool
     smaller and larger than k: every query's pool and indices against the oracle."""
     _say(f"index_full 300 queries, narrow selection instance, P={P} k={k}")
     rng = np.random.default_rng(31)
     lengths = [int(x) for x in rng.integers(1, 3000, 300)]
     _indexer_case(fk, gpu, lengths, 4, 64, P, k, seed=31, lo=-1, hi=1)
+
+
+@pytest.mark.parametrize("P,k", [(64, 96), (64, 40)])
+def test_index_full_two_roles_narrow_instance(fk, gpu, P, k):
+    """200 queries: two selection workgroups per query (pool, positions) in
+    the instance held to 64 VGPRs, short ragged contexts with heavy ties, the
+    pool smaller and larger than k: every query against the oracle."""
+    _say(f"index_full 200 queries, two roles, narrow instance, P={P} k={k}")
+    rng = np.random.default_rng(37)
+    lengths = [int(x) for x in rng.integers(1, 3000, 200)]
+    _indexer_case(fk, gpu, lengths, 4, 64, P, k, seed=37, lo=-1, hi=1)
 
 
 @pytest.mark.parametrize("lo,hi", [(-8, 8), (-1, 1)])
