@@ -5,14 +5,15 @@
 // sparse indexer"; [N] "CSA2: Sharing Main KV, Indexer K, and Top-K Indices
 // Across Layers" (the Full layer scores every visible context token).
 //
-// Queries of one sequence share every key, so q_h . k_t for 16 heads x 16
-// tokens is one v_mfma_f32_16x16x32_bf16 tile per 32 channels: rows = heads
-// (the query fragment, resident in VGPRs), columns = tokens (the key fragment,
-// read from LDS). A lane of the result holds 4 heads of one token; ReLU and the
-// head weights are applied there. The four 16-lane groups' partial sums of two
-// queries x two 16-token tiles are then reduce-scattered with
-// v_permlane32_swap and v_permlane16_swap so that lane l ends with the full
-// score of query l/32 at token l%32 of a 32-token part of the tile.
+// Queries of one sequence share every key, so the q_h . k_t of a wave's four
+// queries over 16 tokens are v_mfma_f32_16x16x32_bf16 tiles per 32 channels:
+// rows = (query, head) pairs (the query fragments, resident in VGPRs), columns =
+// tokens (the key fragment, read from LDS). The rows are arranged so that a
+// result lane holds 4 heads of one query at one token, and the four products
+// over the four groups of 4 heads leave all 16 heads of that query and token
+// in the lane: ReLU, the head weights and the sum over the heads are applied
+// there, with no exchange between lanes, and lane l ends with the score of
+// query l/16 at token l%16 of a 16-token tile.
 //
 // Workgroup = 32 queries of one sequence x one range of tokens: 8 compute waves
 // (4 queries each) and one copy wave. The copy wave streams 128-token key tiles
@@ -23,8 +24,8 @@
 // before it the copy wave has waited for the next tile and the compute waves
 // have finished the current one; the tile after next is then loaded into the
 // slot the finished tile leaves free. Within a tile, each 32-token part's
-// 32 products (both query pairs) are issued before either pair's weighted
-// ReLU sums, so that one pair's vector work overlaps the other's products.
+// 32 products (both 16-token tiles) are issued before either tile's weighted
+// ReLU sums, so that one tile's vector work overlaps the other's products.
 //
 // Work items (query block, token range) are laid out so that the workgroups
 // an XCD runs together share one token range, which then streams through that
@@ -134,45 +135,49 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a, MfmaSc
     return;
   }
 
-  // ---------------- compute waves: queries q0 + 4*wave + j, j = 0..3
+  // ---------------- compute waves: queries q0 + 4*wave + j, j = 0..3.
+  // Product m of a 16-token tile has rows (query j, head 4m + i) at row 4j + i,
+  // so result register i of lane l holds head 4m + i of query l/16 at token
+  // l%16: after the four products m = 0..3 a lane holds all 16 heads of its
+  // query and token, and the weighted ReLU sum over the heads stays inside it.
   const int g4 = lane / 16, col = lane % 16;
-  uint4 qa[4][KS];                            // A operand: Q[q][head col][32ks + 8g4 .. +7]
-  float wv[4][4];                             // w[q][4g4 + i]
+  uint4 qa[4][KS];                            // A operand of product m: Q[q0+4w+col/4][4m + col%4][32ks + 8g4 .. +7]
+  float wv[16];                               // w[query q0+4w+g4][h]
+  {
+    const int qr = q0 + 4 * wave + col / 4;   // this lane's A row query
+    const bool qvalid = qr < q1;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int q = q0 + 4 * wave + j;
-    const bool valid = q < q1;
-    const uint4* qp = reinterpret_cast<const uint4*>(a.idx_q + ((int64_t)(valid ? q : q0) * g.H + (col < g.H ? col : 0)) * D);
+    for (int m = 0; m < 4; ++m) {
+      const int h = 4 * m + col % 4;
+      const bool valid = qvalid && h < g.H;
+      const uint4* qp = reinterpret_cast<const uint4*>(a.idx_q + ((int64_t)(valid ? qr : q0) * g.H + (valid ? h : 0)) * D);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 v = qp[4 * ks + g4];
-      qa[j][ks] = (valid && col < g.H) ? v : make_uint4(0u, 0u, 0u, 0u);
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 v = qp[4 * ks + g4];
+        qa[m][ks] = valid ? v : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
+    const int qw4 = q0 + 4 * wave + g4;       // this lane's result query
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * g4 + i;
-      wv[j][i] = (valid && h < g.H) ? a.w[(int64_t)q * g.H + h] : 0.0f;
-    }
+    for (int h = 0; h < 16; ++h) wv[h] = (qw4 < q1 && h < g.H) ? a.w[(int64_t)qw4 * g.H + h] : 0.0f;
   }
-  // This lane's token of each 32-token part is t0 + 32 part + lane % 32, its
-  // scores belong to query 2jp + lane/32. The wave's four score and
-  // block-maximum rows start at uniform bases; carried from tile to tile are
-  // 32-bit byte offsets from them to that token's score and block maximum in
-  // part 0 (parts add immediate offsets; four rows of max_ctx < 2^28 tokens
-  // keep them below 2^32) and how many of the query's visible tokens lie at or
-  // past it.
+  // This lane's token of each 16-token tile tt of part `part` is t0 + 32 part +
+  // 16 tt + lane % 16, its score belongs to query lane/16 of the wave. The wave's
+  // four score and block-maximum rows start at uniform bases; carried from tile
+  // to tile are 32-bit byte offsets from them to that token's score and block
+  // maximum in part 0, tile 0 (parts and tiles add immediate offsets; four rows
+  // of max_ctx < 2^28 tokens keep them below 2^32) and how many of the query's
+  // visible tokens lie at or past it.
   const int qw = q0 + 4 * __builtin_amdgcn_readfirstlane(wave);
   char* const sbase = reinterpret_cast<char*>(a.scores + (int64_t)qw * a.max_ctx);
   char* const bbase = reinterpret_cast<char*>(a.blockmax + (int64_t)qw * a.nblk_max);
-  uint32_t so[2], bo[2];
-  int32_t rem[2];
-#pragma unroll
-  for (int jp = 0; jp < 2; ++jp) {
-    const int64_t row = 2 * jp + (lane >> 5);
-    const int64_t tb = r0 + (lane & 31);      // r0 is a multiple of 128: tb / 8 is the lane's block
-    so[jp] = (uint32_t)((row * a.max_ctx + tb) * 4);
-    bo[jp] = (uint32_t)((row * a.nblk_max + (tb >> 3)) * 4);
-    rem[jp] = (int32_t)(nvis[4 * wave + row] - tb);
+  uint32_t so, bo;
+  int32_t rem;
+  {
+    const int64_t tb = r0 + col;              // r0 is a multiple of 128: tb / 8 is the lane's block
+    so = (uint32_t)((g4 * a.max_ctx + tb) * 4);
+    bo = (uint32_t)((g4 * a.nblk_max + (tb >> 3)) * 4);
+    rem = (int32_t)(nvis[4 * wave + g4] - tb);
   }
   tile_barrier();
 
@@ -187,62 +192,42 @@ __global__ __launch_bounds__(kMThreads) void scan_mfma_kernel(ScanArgs a, MfmaSc
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) bf[tt][ks] = tile[tok * NCH + ((4 * ks + g4) ^ (tok % NCH))];
       }
-      v4f acc[2][2][2];                       // [query pair jp][query of the pair][16-token tile]
+      v4f acc[2][4];                          // [16-token tile][head group m]
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) acc[jp][qq][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 4; ++m) acc[tt][m] = v4f{0.f, 0.f, 0.f, 0.f};
       // A wave raises its priority while it issues its products, so that the
       // matrix core is fed first and the other waves' vector work fills in
       // around it (measured 2-3% faster than equal priority).
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-              acc[jp][qq][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, qa[2 * jp + qq][ks]),
-                                                                        __builtin_bit_cast(v8bf, bf[tt][ks]),
-                                                                        acc[jp][qq][tt], 0, 0, 0);
+          for (int m = 0; m < 4; ++m)
+            acc[tt][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, qa[m][ks]),
+                                                                 __builtin_bit_cast(v8bf, bf[tt][ks]),
+                                                                 acc[tt][m], 0, 0, 0);
       __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {
-        // lane: heads 4g4..4g4+3 of token col; weighted ReLU sum over them
-        float p[2][2];
+      for (int tt = 0; tt < 2; ++tt) {
+        // lane: all 16 heads of query lane/16 at token col; weighted ReLU sum over them
+        float y = 0.0f;
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            float v = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v = fmaf(wv[2 * jp + qq][i], relu_f(acc[jp][qq][tt][i]), v);
-            p[qq][tt] = v;
-          }
-        // lanes 0-31 <- query A, lanes 32-63 <- query B (head groups g, g+2 summed)
-        const auto xa = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0][0]), __float_as_uint(p[1][0]), false, false);
-        const auto xb = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0][1]), __float_as_uint(p[1][1]), false, false);
-        const float sa = __uint_as_float(xa[0]) + __uint_as_float(xa[1]);
-        const float sb = __uint_as_float(xb[0]) + __uint_as_float(xb[1]);
-        // rows of 16 lanes: (A, tile 0), (A, tile 1), (B, tile 0), (B, tile 1); all four head groups summed
-        const auto yy = __builtin_amdgcn_permlane16_swap(__float_as_uint(sa), __float_as_uint(sb), false, false);
-        const float y = __uint_as_float(yy[0]) + __uint_as_float(yy[1]);
-        const bool vis = 32 * part < rem[jp];
-        if (vis) reinterpret_cast<float*>(sbase + so[jp])[32 * part] = y;
+          for (int i = 0; i < 4; ++i) y = fmaf(wv[4 * m + i], relu_f(acc[tt][m][i]), y);
+        const bool vis = 32 * part + 16 * tt < rem;
+        if (vis) reinterpret_cast<float*>(sbase + so)[32 * part + 16 * tt] = y;
         const float bm = max8(vis ? y : -3.402823466e38f);
-        if ((lane & 7) == 0 && vis) reinterpret_cast<float*>(bbase + bo[jp])[4 * part] = bm;
+        if ((lane & 7) == 0 && vis) reinterpret_cast<float*>(bbase + bo)[4 * part + 2 * tt] = bm;
       }
     }
-#pragma unroll
-    for (int jp = 0; jp < 2; ++jp) {
-      so[jp] += kMTile * 4;
-      bo[jp] += kMTile / 8 * 4;
-      rem[jp] -= kMTile;
-    }
+    so += kMTile * 4;
+    bo += kMTile / 8 * 4;
+    rem -= kMTile;
     tile_barrier();
   }
 }
