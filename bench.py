@@ -53,8 +53,8 @@ KERNEL_SOURCES = ("api.hip", "attn.hip", "attn_common.h", "common.h", "kernels.h
 # HBM bytes from rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated against a copy of known size:
 # one decode128k step (scan carrying the append, selection, attention, combine) and one scan
 # launch as the breakdown pass times it. Valid only for the kernel sources they were taken on.
-STEP_TRAFFIC = {"sources_sha256_16": "dcd40387079cf9b1", "bytes_per_step": 1191131215,
-                "scan_bytes_per_launch": 1095360329}
+STEP_TRAFFIC = {"sources_sha256_16": "d329774a791f307c", "bytes_per_step": 1191144682,
+                "scan_bytes_per_launch": 1095364563}
 
 
 def log(msg):
