@@ -27,7 +27,9 @@ Prints one JSON line: the metric (queries/s), the step time, the roofline of
 the layer (its compulsory HBM bytes over the measured step time, against
 8 TB/s, with the HBM traffic the byte counters measured) and, inside it, that
 of its dominant kernel (the indexer scan), and the float64 oracle's rate on the
-host cores as a CPU baseline.
+host cores as a CPU baseline. The record's detail carries a SHA-256 of the
+generated inputs (every tensor the step reads, taken before the first step),
+so that runs on different boxes can be checked to have used the same bytes.
 """
 from __future__ import annotations
 
@@ -102,6 +104,25 @@ def sources_hash():
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "sparse_indexer_fp4_amd", "csrc", name), "rb") as f:
             h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def inputs_sha256(named):
+    """SHA-256 (first 16 hex digits) of generated inputs: each tensor's name,
+    dtype and shape, then its bytes, in the given order. Tensors are copied to
+    the host in 64 MiB pieces; this runs before the untimed warm-up."""
+    import hashlib
+    import torch
+    h = hashlib.sha256()
+    piece = 64 << 20
+    for name, t in named:
+        if t is None:
+            continue
+        t = t.contiguous()
+        h.update(f"{name}:{t.dtype}:{tuple(t.shape)};".encode())
+        flat = t.reshape(-1).view(torch.uint8)
+        for i in range(0, flat.numel(), piece):
+            h.update(memoryview(flat[i:i + piece].cpu().numpy()))
     return h.hexdigest()[:16]
 
 
@@ -316,6 +337,13 @@ def run_workload(args, name):
     new_x, new_dst = dw.appended_rows() if cfg.kind == "mixed" else (None, None)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    named = [("idx_k", dw.idx_k), ("codes", dw.codes), ("scales", dw.scales), ("seq_start", dw.seq_start),
+             ("q_pos", dw.q_pos), ("new_x", new_x), ("new_dst", new_dst)]
+    for layer in range(len(modes)):
+        named += [(f"q{layer}", dw.q[layer]), (f"swa_k{layer}", dw.swa_k[layer]), (f"swa_v{layer}", dw.swa_v[layer]),
+                  (f"idx_q{layer}", dw.idx_q.get(layer)), (f"w{layer}", dw.w.get(layer))]
+    in_hash = inputs_sha256(named)
+    log(f"inputs hashed: {in_hash}")
     stream = torch.cuda.current_stream()
 
     def step(scan_ev):
@@ -392,7 +420,8 @@ def run_workload(args, name):
         "config": {"workload": WORKLOAD_TEXT[name], "queries": B, "max_ctx": max_ctx, "layers": len(modes),
                    "parallelism": "single GPU"},
         "roofline": roof,
-        "detail": {"scan_ms_timed_region": scan_ms},
+        "detail": {"scan_ms_timed_region": scan_ms, "inputs_sha256_16": in_hash,
+                   "kernel_sources_sha256_16": sources_hash()},
         "cpu_baseline": None,
     }
     if args.cpu_sample > 0:
@@ -473,6 +502,11 @@ def main():
                       device=dev)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    in_hash = inputs_sha256([("idx_k", dw.idx_k), ("codes", codes), ("scales", scales), ("seq_start", dw.seq_start),
+                             ("q_pos", dw.q_pos), ("idx_q", dw.idx_q[0]), ("w", dw.w[0]), ("q", dw.q[0]),
+                             ("swa_k", dw.swa_k[0]), ("swa_v", dw.swa_v[0]), ("new_x", new_x),
+                             ("new_dst", new_dst)])
+    log(f"inputs hashed: {in_hash}")
 
     stream = torch.cuda.current_stream()
 
@@ -582,7 +616,7 @@ def main():
                          "timing": "HIP events around the scan in an untimed pass of the same step as "
                                    "separate launches"}},
         "detail": {"ms_per_launch": per, "ms_per_step_events": ms_step_events, "algorithmic_bytes": nbytes,
-                   "kernel_sources_sha256_16": sources_hash()},
+                   "inputs_sha256_16": in_hash, "kernel_sources_sha256_16": sources_hash()},
     }
     if args.cpu_sample > 0:
         log(f"timing the oracle on {args.cpu_sample} queries")

@@ -73,3 +73,32 @@ def test_kernel_sources_cover_every_source_file():
     csrc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "sparse_indexer_fp4_amd", "csrc")
     on_disk = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
     assert sorted(bench.KERNEL_SOURCES) == on_disk
+
+
+def test_inputs_hash_covers_names_shapes_bytes_and_order():
+    """The input digest is SHA-256 over (name, dtype, shape) headers and the raw
+    bytes, in order; a changed byte, shape, name or order changes it, and a
+    missing (None) tensor is skipped. Tensors larger than one 64 MiB piece are
+    hashed piece by piece to the same digest."""
+    import hashlib
+    import torch
+    x = torch.arange(10, dtype=torch.bfloat16)
+    y = torch.arange(6, dtype=torch.int64).reshape(2, 3)
+    h = hashlib.sha256()
+    h.update(b"x:torch.bfloat16:(10,);")
+    h.update(x.view(torch.uint8).numpy().tobytes())
+    h.update(b"y:torch.int64:(2, 3);")
+    h.update(y.reshape(-1).view(torch.uint8).numpy().tobytes())
+    base = bench.inputs_sha256([("x", x), ("gone", None), ("y", y)])
+    assert base == h.hexdigest()[:16]
+    x2 = x.clone()
+    x2[3] = 100.0
+    assert bench.inputs_sha256([("x", x2), ("y", y)]) != base
+    assert bench.inputs_sha256([("x", x), ("y", y.reshape(3, 2))]) != base
+    assert bench.inputs_sha256([("x", x), ("z", y)]) != base
+    assert bench.inputs_sha256([("y", y), ("x", x)]) != base
+    big = torch.arange((64 << 20) // 4 + 5, dtype=torch.int32)
+    hb = hashlib.sha256()
+    hb.update(f"big:torch.int32:{tuple(big.shape)};".encode())
+    hb.update(big.numpy().tobytes())
+    assert bench.inputs_sha256([("big", big)]) == hb.hexdigest()[:16]
