@@ -409,6 +409,22 @@ def test_index_full_many_queries_narrow_selection(fk, gpu, P, k):
     _indexer_case(fk, gpu, lengths, 4, 64, P, k, seed=31, lo=-1, hi=1)
 
 
+@pytest.mark.parametrize("P,k,lo,hi", [
+    (1024, 2048, -8, 8),    # pool of 1,024 blocks, smaller than k: all of its positions searched
+    (2048, 1024, -8, 8),    # k = 1,024 best blocks of the pool
+    (2048, 1024, -1, 1),    # the same with heavy ties
+])
+def test_index_full_wide_token_search(fk, gpu, P, k, lo, hi):
+    """More than 512 blocks reach the token search, so each thread holds 16
+    candidates (two blocks): few queries (two workgroups per query) and 260
+    queries of one sequence (one workgroup per query, the pool narrowed to k)."""
+    _say(f"index_full wide token search P={P} k={k} values {lo}..{hi}")
+    _indexer_case(fk, gpu, [30000, 20001, 12345], 4, 64, P, k, seed=71, lo=lo, hi=hi)
+    rng = np.random.default_rng(73)
+    positions = sorted(int(x) for x in rng.integers(9000, 30000, 260))
+    _indexer_case(fk, gpu, [30000], 4, 64, P, k, seed=73, lo=lo, hi=hi, q_per_seq=260, positions=positions)
+
+
 @pytest.mark.parametrize("P,k", [(64, 96), (64, 40)])
 def test_index_full_two_roles_narrow_instance(fk, gpu, P, k):
     """200 queries: two selection workgroups per query (pool, positions) in
